@@ -1,0 +1,276 @@
+/*
+ * Lightning-indexer oracle: a plain, slow, obviously correct CPU reference.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file or the library built from it; only the tests, the
+ * smoke check and the benchmark's CPU-baseline leg use it.  It shares no
+ * code, header, table or helper with the HIP library.
+ *
+ * What it computes (llama.cpp release b11372, "qwen4exp: halve the indexer
+ * score memory" and "qwen4exp: compute the indexer score with the lightning
+ * indexer"; vLLM PR #45743, "Tune Triton indexer score decode for
+ * spec-decode", kernel section):
+ *
+ *   score[t][s] = sum over heads h of  w[h] * max(q[t][h][:] . k[s][:], 0)
+ *                 + mask[t][s]
+ *
+ * Each head's dot product is rectified on its own and only then summed (the
+ * b11372 notes: every head gets its own product, rectified, then summed in
+ * place into one [n_pool, n_tokens] score).  Any 1/sqrt(head_dim) scale is
+ * carried in w (the notes on the lightning indexer: the scaled unweighted sum
+ * is the indexer with every head weight set to the scale; the vLLM decode
+ * kernel drops sm_scale).  Keys are shared by every head.  The f16 mask is
+ * additive and enters once, after the head sum; an entry whose mask is -inf,
+ * or which lies past the row's visible length, is invisible and scores -inf.
+ *
+ * Arithmetic: every f16 and f32 input is widened exactly to double and all
+ * products and sums are formed in double, in the natural index order.
+ *
+ * Top-k (the selection step of the vLLM index_topk module): for every row,
+ * the k_top visible keys with the largest score, ordered by score descending
+ * and, among equal scores, by key index ascending; -inf and NaN are never
+ * selected and -0 ties with +0.  Rows with fewer than k_top visible keys are
+ * padded with index -1 and value -inf.
+ *
+ * Pins: every function here is checked by tests/test_oracle_pins.py against
+ * a hand-derived worked example, closed forms, the pages' scale identity, the
+ * "materialise then sum" scheme the pages replaced, a sign-flip identity that
+ * reduces to a plain matrix product, and a library sort.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+/* IEEE 754 binary16 -> double, from the format's definition: 1 sign bit,
+ * 5 exponent bits (bias 15), 10 fraction bits. */
+static double half_to_double(uint16_t h)
+{
+    int sign = (h >> 15) & 1;
+    int expo = (h >> 10) & 0x1f;
+    int frac = h & 0x3ff;
+    double v;
+    if (expo == 0)
+        v = ldexp((double)frac, -24);            /* zero or subnormal */
+    else if (expo == 31)
+        v = frac ? NAN : INFINITY;               /* inf or NaN */
+    else
+        v = ldexp((double)(frac + 1024), expo - 25);
+    return sign ? -v : v;
+}
+
+static int half_is_neg_inf(uint16_t h) { return h == 0xfc00; }
+
+/* One visible (token, key) pair: rectify each head, weight, sum. */
+static double head_sum(const uint16_t *q_t, int64_t q_stride_h,
+                       const uint16_t *k_s, const float *w, int H, int d)
+{
+    double total = 0.0;
+    for (int h = 0; h < H; ++h) {
+        const uint16_t *q_th = q_t + (int64_t)h * q_stride_h;
+        double dot = 0.0;
+        for (int i = 0; i < d; ++i)
+            dot += half_to_double(q_th[i]) * half_to_double(k_s[i]);
+        double rect = dot > 0.0 ? dot : 0.0;
+        total += (double)w[h] * rect;
+    }
+    return total;
+}
+
+/*
+ * Contiguous ("prefill") score.
+ *   q    f16 [T][H][d] with strides (q_stride_t, q_stride_h, 1) in elements
+ *   k    f16 [P][d]    with stride k_stride_s
+ *   w    f32 [H]
+ *   mask f16 [T][P] with stride mask_stride_t, or NULL (all visible, +0)
+ *   vis_len i32 [T]: key s is visible to token t only if s < vis_len[t];
+ *        NULL means every s < P
+ *   out  f64 [T][P] with stride out_stride_t
+ */
+void oracle_score_prefill(const uint16_t *q, int64_t q_stride_t, int64_t q_stride_h,
+                          const uint16_t *k, int64_t k_stride_s,
+                          const float *w,
+                          const uint16_t *mask, int64_t mask_stride_t,
+                          const int32_t *vis_len,
+                          int T, int P, int H, int d,
+                          double *out, int64_t out_stride_t)
+{
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int t = 0; t < T; ++t) {
+        for (int s = 0; s < P; ++s) {
+            double *o = out + (int64_t)t * out_stride_t + s;
+            int visible = 1;
+            if (vis_len && s >= vis_len[t])
+                visible = 0;
+            if (mask && half_is_neg_inf(mask[(int64_t)t * mask_stride_t + s]))
+                visible = 0;
+            if (!visible) {
+                *o = -INFINITY;
+                continue;
+            }
+            double v = head_sum(q + (int64_t)t * q_stride_t, q_stride_h,
+                                k + (int64_t)s * k_stride_s, w, H, d);
+            if (mask)
+                v += half_to_double(mask[(int64_t)t * mask_stride_t + s]);
+            *o = v;
+        }
+    }
+}
+
+/*
+ * Paged ("decode") score.  Request r owns query rows r*Q .. r*Q+Q-1 (query j
+ * of request r is row r*Q+j) and keys 0 .. seq_lens[r]-1.  Logical key s of
+ * request r lives in physical block block_table[r*bt_stride + s/block_size],
+ * slot s % block_size, of k_cache [n_blocks][block_size][d].
+ *
+ * Query j is the (j+1)-th of Q trailing tokens of the request, so it sees the
+ * keys before the speculative tail plus the accepted ones up to itself:
+ * s < seq_len - Q + 1 + j (for Q = 1: every s < seq_len).
+ *
+ *   mask f16 [R*Q][max_seq_len] with stride mask_stride_t, or NULL
+ *   out  f64 [R*Q][max_seq_len] with stride out_stride_t; keys at or past the
+ *        row's visible length score -inf.
+ */
+void oracle_score_decode(const uint16_t *q, int64_t q_stride_t, int64_t q_stride_h,
+                         const uint16_t *k_cache, int block_size,
+                         const int32_t *block_table, int64_t bt_stride,
+                         const int32_t *seq_lens,
+                         int R, int Q, int max_seq_len,
+                         const float *w,
+                         const uint16_t *mask, int64_t mask_stride_t,
+                         int H, int d,
+                         double *out, int64_t out_stride_t)
+{
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    for (int r = 0; r < R; ++r) {
+        for (int j = 0; j < Q; ++j) {
+            int64_t t = (int64_t)r * Q + j;
+            int64_t vis = (int64_t)seq_lens[r] - Q + 1 + j;
+            if (vis > max_seq_len)
+                vis = max_seq_len;
+            for (int s = 0; s < max_seq_len; ++s) {
+                double *o = out + t * out_stride_t + s;
+                int visible = s < vis;
+                if (visible && mask && half_is_neg_inf(mask[t * mask_stride_t + s]))
+                    visible = 0;
+                if (!visible) {
+                    *o = -INFINITY;
+                    continue;
+                }
+                int64_t phys = block_table[(int64_t)r * bt_stride + s / block_size];
+                const uint16_t *k_s = k_cache + (phys * block_size + s % block_size) * (int64_t)d;
+                double v = head_sum(q + t * q_stride_t, q_stride_h, k_s, w, H, d);
+                if (mask)
+                    v += half_to_double(mask[t * mask_stride_t + s]);
+                *o = v;
+            }
+        }
+    }
+}
+
+/* ---------------------------- top-k ----------------------------------- */
+
+typedef struct {
+    double score;
+    int32_t index;
+} cand_t;
+
+/* Total order: larger score first; equal scores (with -0 == +0) by smaller
+ * key index first. */
+static int cand_cmp(const void *a, const void *b)
+{
+    const cand_t *x = (const cand_t *)a, *y = (const cand_t *)b;
+    if (x->score > y->score) return -1;
+    if (x->score < y->score) return 1;
+    return (x->index > y->index) - (x->index < y->index);
+}
+
+static void topk_row(const double *row, int n, int k_top, cand_t *scratch,
+                     int32_t *idx_out, double *val_out)
+{
+    int m = 0;
+    for (int s = 0; s < n; ++s) {
+        double v = row[s];
+        if (isnan(v) || (isinf(v) && v < 0))
+            continue;                          /* never selectable */
+        scratch[m].score = v == 0.0 ? 0.0 : v; /* -0 -> +0 */
+        scratch[m].index = s;
+        ++m;
+    }
+    qsort(scratch, (size_t)m, sizeof(cand_t), cand_cmp);
+    for (int i = 0; i < k_top; ++i) {
+        if (i < m) {
+            idx_out[i] = scratch[i].index;
+            if (val_out) val_out[i] = row[scratch[i].index];
+        } else {
+            idx_out[i] = -1;
+            if (val_out) val_out[i] = -INFINITY;
+        }
+    }
+}
+
+/*
+ * Top-k over double score rows [n_rows][n_cols] (stride score_stride).
+ * row_len i32 [n_rows] limits row t to its first row_len[t] columns, or NULL.
+ * idx_out i32 [n_rows][k_top], val_out f64 [n_rows][k_top] (nullable).
+ */
+void oracle_topk_f64(const double *score, int64_t score_stride, int n_rows, int n_cols,
+                     const int32_t *row_len, int k_top,
+                     int32_t *idx_out, double *val_out)
+{
+#pragma omp parallel
+    {
+        cand_t *scratch = (cand_t *)malloc(sizeof(cand_t) * (size_t)(n_cols > 0 ? n_cols : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int t = 0; t < n_rows; ++t) {
+            int n = n_cols;
+            if (row_len && row_len[t] < n) n = row_len[t] < 0 ? 0 : row_len[t];
+            topk_row(score + (int64_t)t * score_stride, n, k_top, scratch,
+                     idx_out + (int64_t)t * k_top,
+                     val_out ? val_out + (int64_t)t * k_top : NULL);
+        }
+        free(scratch);
+    }
+}
+
+/* Same selection over f32 score rows (e.g. scores produced elsewhere); each
+ * f32 is widened exactly to double, so the order is the f32 order. */
+void oracle_topk_f32(const float *score, int64_t score_stride, int n_rows, int n_cols,
+                     const int32_t *row_len, int k_top,
+                     int32_t *idx_out, float *val_out)
+{
+#pragma omp parallel
+    {
+        cand_t *scratch = (cand_t *)malloc(sizeof(cand_t) * (size_t)(n_cols > 0 ? n_cols : 1));
+        double *row = (double *)malloc(sizeof(double) * (size_t)(n_cols > 0 ? n_cols : 1));
+        double *vals = (double *)malloc(sizeof(double) * (size_t)(k_top > 0 ? k_top : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int t = 0; t < n_rows; ++t) {
+            int n = n_cols;
+            if (row_len && row_len[t] < n) n = row_len[t] < 0 ? 0 : row_len[t];
+            const float *src = score + (int64_t)t * score_stride;
+            for (int s = 0; s < n; ++s) row[s] = (double)src[s];
+            topk_row(row, n, k_top, scratch, idx_out + (int64_t)t * k_top,
+                     val_out ? vals : NULL);
+            if (val_out)
+                for (int i = 0; i < k_top; ++i)
+                    val_out[(int64_t)t * k_top + i] = (float)vals[i];
+        }
+        free(vals);
+        free(row);
+        free(scratch);
+    }
+}
+
+/* Number of threads the OpenMP loops above run with (1 without OpenMP). */
+int oracle_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}

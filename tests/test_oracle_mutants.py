@@ -1,0 +1,69 @@
+"""Plant plausible mistakes in copies of the oracle source and check that the
+pin suite catches every one of them (on the CPU; the real oracle is untouched).
+"""
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+import oracle
+
+_RUNNER = """
+import json, sys
+sys.path[:0] = [{root!r}, {tests!r}]
+import oracle
+from oracle_pins import ALL_PINS
+lib = oracle.load({so!r})
+failed = []
+for pin in ALL_PINS:
+    try:
+        pin(lib)
+    except Exception:
+        failed.append(pin.__name__)
+print(json.dumps(failed))
+"""
+
+# (name, text in oracle/indexer_oracle.c, replacement)
+MUTANTS = [
+    ("no_relu", "double rect = dot > 0.0 ? dot : 0.0;", "double rect = dot;"),
+    ("sum_then_relu", "total += (double)w[h] * rect;", "total += (double)w[h] * dot;"),
+    ("wrong_weight_index", "total += (double)w[h] * rect;", "total += (double)w[0] * rect;"),
+    ("key_index_shift", "half_to_double(k_s[i])", "half_to_double(k_s[(i + 1) % d])"),
+    ("key_dot_reversed", "half_to_double(k_s[i])", "half_to_double(k_s[d - 1 - i])"),
+    ("mask_inside_relu", "            if (mask)\n                v += half_to_double(mask[(int64_t)t * mask_stride_t + s]);",
+     "            if (mask)\n                v = fmax(v + half_to_double(mask[(int64_t)t * mask_stride_t + s]), 0.0);"),
+    ("mask_dropped", "            if (mask)\n                v += half_to_double(mask[(int64_t)t * mask_stride_t + s]);", ""),
+    ("f16_bias_off_by_one", "expo - 25", "expo - 24"),
+    ("f16_subnormal_wrong", "ldexp((double)frac, -24)", "ldexp((double)frac, -25)"),
+    ("ties_to_higher_index", "return (x->index > y->index) - (x->index < y->index);",
+     "return (x->index < y->index) - (x->index > y->index);"),
+    ("neg_inf_selectable", "if (isnan(v) || (isinf(v) && v < 0))", "if (isnan(v))"),
+    ("ascending_order", "if (x->score > y->score) return -1;\n    if (x->score < y->score) return 1;",
+     "if (x->score < y->score) return -1;\n    if (x->score > y->score) return 1;"),
+    ("no_padding", "idx_out[i] = -1;", "idx_out[i] = 0;"),
+    ("decode_visibility_off_by_one", "(int64_t)seq_lens[r] - Q + 1 + j", "(int64_t)seq_lens[r] - Q + j"),
+    ("decode_ignores_block_table", "(phys * block_size + s % block_size)", "((int64_t)s)"),
+    ("decode_first_block_only", "s / block_size];", "0];"),
+]
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_mutant(name, old, new, tmp_path):
+    src = open(oracle.SRC).read()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    mutated = src.replace(old, new)
+    path = tmp_path / "mutant.c"
+    path.write_text(mutated)
+    so = str(tmp_path / "libmutant.so")
+    oracle.build(str(path), so, extra_flags=("-w",))
+    tests = os.path.dirname(os.path.abspath(__file__))
+    code = _RUNNER.format(root=os.path.dirname(tests), tests=tests, so=so)
+    # each mutant runs in its own process so that a planted mistake cannot
+    # disturb the test process
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True,
+                         text=True, timeout=300)
+    assert res.returncode == 0, f"mutant {name} crashed: {res.stderr[-400:]}"
+    failed = json.loads(res.stdout.strip().splitlines()[-1])
+    assert failed, f"mutant {name} survived every pin"

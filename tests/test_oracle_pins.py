@@ -1,0 +1,10 @@
+"""The CPU oracle against its pins (worked examples, closed forms, the pages'
+scale identity, the materialise-then-sum scheme, library sorts)."""
+import pytest
+
+from oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_oracle_pin(pin, oracle_lib):
+    pin(oracle_lib)
