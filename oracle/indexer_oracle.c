@@ -64,16 +64,39 @@ static double half_to_double(uint16_t h)
 
 static int half_is_neg_inf(uint16_t h) { return h == 0xfc00; }
 
-/* One visible (token, key) pair: rectify each head, weight, sum. */
-static double head_sum(const uint16_t *q_t, int64_t q_stride_h,
-                       const uint16_t *k_s, const float *w, int H, int d)
+/* Widen rows of f16 values to a dense double array [n_rows][d]. */
+static double *widen_rows(const uint16_t *src, int64_t n_rows, int64_t row_stride, int d)
+{
+    double *dst = (double *)malloc(sizeof(double) * (size_t)(n_rows > 0 ? n_rows : 1) * (size_t)d);
+    for (int64_t r = 0; r < n_rows; ++r)
+        for (int i = 0; i < d; ++i)
+            dst[r * d + i] = half_to_double(src[r * row_stride + i]);
+    return dst;
+}
+
+/* Widen q [T][H][d] (strides q_stride_t, q_stride_h) to dense [T][H][d]. */
+static double *widen_queries(const uint16_t *q, int64_t q_stride_t, int64_t q_stride_h,
+                             int T, int H, int d)
+{
+    double *dst = (double *)malloc(sizeof(double) * (size_t)(T > 0 ? T : 1) * (size_t)H * (size_t)d);
+    for (int t = 0; t < T; ++t)
+        for (int h = 0; h < H; ++h)
+            for (int i = 0; i < d; ++i)
+                dst[((int64_t)t * H + h) * d + i] =
+                    half_to_double(q[(int64_t)t * q_stride_t + (int64_t)h * q_stride_h + i]);
+    return dst;
+}
+
+/* One visible (token, key) pair: rectify each head's dot product, weight it,
+ * sum over heads.  q_t is [H][d], k_s is [d], both already in double. */
+static double head_sum(const double *q_t, const double *k_s, const float *w, int H, int d)
 {
     double total = 0.0;
     for (int h = 0; h < H; ++h) {
-        const uint16_t *q_th = q_t + (int64_t)h * q_stride_h;
+        const double *q_th = q_t + (int64_t)h * d;
         double dot = 0.0;
         for (int i = 0; i < d; ++i)
-            dot += half_to_double(q_th[i]) * half_to_double(k_s[i]);
+            dot += q_th[i] * k_s[i];
         double rect = dot > 0.0 ? dot : 0.0;
         total += (double)w[h] * rect;
     }
@@ -98,6 +121,8 @@ void oracle_score_prefill(const uint16_t *q, int64_t q_stride_t, int64_t q_strid
                           int T, int P, int H, int d,
                           double *out, int64_t out_stride_t)
 {
+    double *qd = widen_queries(q, q_stride_t, q_stride_h, T, H, d);
+    double *kd = widen_rows(k, P, k_stride_s, d);
 #pragma omp parallel for schedule(dynamic, 1) collapse(2)
     for (int t = 0; t < T; ++t) {
         for (int s = 0; s < P; ++s) {
@@ -111,13 +136,14 @@ void oracle_score_prefill(const uint16_t *q, int64_t q_stride_t, int64_t q_strid
                 *o = -INFINITY;
                 continue;
             }
-            double v = head_sum(q + (int64_t)t * q_stride_t, q_stride_h,
-                                k + (int64_t)s * k_stride_s, w, H, d);
+            double v = head_sum(qd + (int64_t)t * H * d, kd + (int64_t)s * d, w, H, d);
             if (mask)
                 v += half_to_double(mask[(int64_t)t * mask_stride_t + s]);
             *o = v;
         }
     }
+    free(kd);
+    free(qd);
 }
 
 /*
@@ -144,31 +170,41 @@ void oracle_score_decode(const uint16_t *q, int64_t q_stride_t, int64_t q_stride
                          int H, int d,
                          double *out, int64_t out_stride_t)
 {
-#pragma omp parallel for schedule(dynamic, 1) collapse(2)
+    double *qd = widen_queries(q, q_stride_t, q_stride_h, R * Q, H, d);
     for (int r = 0; r < R; ++r) {
+        int L = seq_lens[r] < max_seq_len ? seq_lens[r] : max_seq_len;
+        if (L < 0)
+            L = 0;
+        /* fetch the request's keys through its block table */
+        double *kd = (double *)malloc(sizeof(double) * (size_t)(L > 0 ? L : 1) * (size_t)d);
+        for (int s = 0; s < L; ++s) {
+            int64_t phys = block_table[(int64_t)r * bt_stride + s / block_size];
+            const uint16_t *k_s = k_cache + (phys * block_size + s % block_size) * (int64_t)d;
+            for (int i = 0; i < d; ++i)
+                kd[(int64_t)s * d + i] = half_to_double(k_s[i]);
+        }
+#pragma omp parallel for schedule(dynamic, 1) collapse(2)
         for (int j = 0; j < Q; ++j) {
-            int64_t t = (int64_t)r * Q + j;
-            int64_t vis = (int64_t)seq_lens[r] - Q + 1 + j;
-            if (vis > max_seq_len)
-                vis = max_seq_len;
             for (int s = 0; s < max_seq_len; ++s) {
+                int64_t t = (int64_t)r * Q + j;
+                int64_t vis = (int64_t)seq_lens[r] - Q + 1 + j;
                 double *o = out + t * out_stride_t + s;
-                int visible = s < vis;
+                int visible = s < vis && s < L;
                 if (visible && mask && half_is_neg_inf(mask[t * mask_stride_t + s]))
                     visible = 0;
                 if (!visible) {
                     *o = -INFINITY;
                     continue;
                 }
-                int64_t phys = block_table[(int64_t)r * bt_stride + s / block_size];
-                const uint16_t *k_s = k_cache + (phys * block_size + s % block_size) * (int64_t)d;
-                double v = head_sum(q + t * q_stride_t, q_stride_h, k_s, w, H, d);
+                double v = head_sum(qd + t * H * d, kd + (int64_t)s * d, w, H, d);
                 if (mask)
                     v += half_to_double(mask[t * mask_stride_t + s]);
                 *o = v;
             }
         }
+        free(kd);
     }
+    free(qd);
 }
 
 /* ---------------------------- top-k ----------------------------------- */

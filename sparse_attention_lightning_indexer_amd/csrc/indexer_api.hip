@@ -1,0 +1,378 @@
+// C-ABI of the lightning-indexer library (declared in include/indexer.h).
+//
+// Every entry point validates its arguments on the host before it enqueues
+// anything; the checks touch no device memory and make no HIP call, so the
+// error paths run without a GPU.  Kernels are enqueued on the caller's
+// stream; the library allocates nothing.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <mutex>
+
+#include "../../include/indexer.h"
+#include "internal.h"
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+indexer_status fail(indexer_status st, const char *fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_last_error, sizeof g_last_error, fmt, ap);
+    va_end(ap);
+    return st;
+}
+
+indexer_status ok() {
+    g_last_error[0] = '\0';
+    return INDEXER_OK;
+}
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+indexer_status hip_status(hipError_t e, const char *what) {
+    if (e == hipSuccess) return ok();
+    return fail(INDEXER_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int log2_exact(int v) {
+    if (v <= 0 || (v & (v - 1))) return -1;
+    int s = 0;
+    while ((1 << s) < v) ++s;
+    return s;
+}
+
+size_t round_up(size_t v, size_t m) { return (v + m - 1) / m * m; }
+
+// Checks shared by the prefill and decode score entry points.
+indexer_status check_q_w(const void *q, int64_t q_stride_t, int64_t q_stride_h, const float *w,
+                         int32_t n_heads, int32_t head_dim) {
+    if (!lidx::score_shape_supported(n_heads, head_dim))
+        return fail(INDEXER_ENOTSUP, "n_heads=%d head_dim=%d not supported (n_heads in {4,8,16,32,64}, head_dim in {64,128})",
+                    n_heads, head_dim);
+    if (!q) return fail(INDEXER_EINVAL, "q is NULL");
+    if (!w) return fail(INDEXER_EINVAL, "w is NULL");
+    if (!aligned(q, 16)) return fail(INDEXER_EINVAL, "q must be 16-byte aligned");
+    if (!aligned(w, 4)) return fail(INDEXER_EINVAL, "w must be 4-byte aligned");
+    if (q_stride_h < head_dim || q_stride_h % 8)
+        return fail(INDEXER_EINVAL, "q_stride_h=%lld must be >= head_dim and a multiple of 8", (long long)q_stride_h);
+    if (q_stride_t < head_dim || q_stride_t % 8)
+        return fail(INDEXER_EINVAL, "q_stride_t=%lld must be >= head_dim and a multiple of 8", (long long)q_stride_t);
+    return INDEXER_OK;
+}
+
+indexer_status check_prefill(const void *q, int64_t q_stride_t, int64_t q_stride_h, const void *k,
+                             int64_t k_stride_s, const float *w, const void *mask, int64_t mask_stride_t,
+                             const int32_t *vis_len, int32_t n_tokens, int32_t n_pool, int32_t n_heads,
+                             int32_t head_dim) {
+    if (n_tokens < 0 || n_pool < 0)
+        return fail(INDEXER_EINVAL, "n_tokens=%d n_pool=%d must be >= 0", n_tokens, n_pool);
+    indexer_status st = check_q_w(q, q_stride_t, q_stride_h, w, n_heads, head_dim);
+    if (st != INDEXER_OK) return st;
+    if (!k) return fail(INDEXER_EINVAL, "k is NULL");
+    if (!aligned(k, 16)) return fail(INDEXER_EINVAL, "k must be 16-byte aligned");
+    if (k_stride_s < head_dim || k_stride_s % 8)
+        return fail(INDEXER_EINVAL, "k_stride_s=%lld must be >= head_dim and a multiple of 8", (long long)k_stride_s);
+    if (mask) {
+        if (!aligned(mask, 2)) return fail(INDEXER_EINVAL, "mask must be 2-byte aligned");
+        if (mask_stride_t < n_pool)
+            return fail(INDEXER_EINVAL, "mask_stride_t=%lld < n_pool=%d", (long long)mask_stride_t, n_pool);
+    }
+    if (vis_len && !aligned(vis_len, 4)) return fail(INDEXER_EINVAL, "vis_len must be 4-byte aligned");
+    return INDEXER_OK;
+}
+
+indexer_status check_decode(const void *q, int64_t q_stride_t, int64_t q_stride_h, const void *k_cache,
+                            int32_t block_size, int64_t k_stride_s, const int32_t *block_table,
+                            int64_t bt_stride, const int32_t *seq_lens, int32_t n_requests,
+                            int32_t query_len, int32_t max_seq_len, const float *w, const void *mask,
+                            int64_t mask_stride_t, int32_t n_heads, int32_t head_dim) {
+    if (n_requests < 0 || max_seq_len < 0)
+        return fail(INDEXER_EINVAL, "n_requests=%d max_seq_len=%d must be >= 0", n_requests, max_seq_len);
+    if (query_len < 1) return fail(INDEXER_EINVAL, "query_len=%d must be >= 1", query_len);
+    if ((int64_t)n_requests * query_len > INT32_MAX)
+        return fail(INDEXER_EINVAL, "n_requests*query_len exceeds the int32 row range");
+    indexer_status st = check_q_w(q, q_stride_t, q_stride_h, w, n_heads, head_dim);
+    if (st != INDEXER_OK) return st;
+    if (!k_cache) return fail(INDEXER_EINVAL, "k_cache is NULL");
+    if (!block_table) return fail(INDEXER_EINVAL, "block_table is NULL");
+    if (!seq_lens) return fail(INDEXER_EINVAL, "seq_lens is NULL");
+    if (!aligned(k_cache, 16)) return fail(INDEXER_EINVAL, "k_cache must be 16-byte aligned");
+    if (!aligned(block_table, 4) || !aligned(seq_lens, 4))
+        return fail(INDEXER_EINVAL, "block_table and seq_lens must be 4-byte aligned");
+    if (block_size < 1) return fail(INDEXER_EINVAL, "block_size=%d must be >= 1", block_size);
+    if (k_stride_s < head_dim || k_stride_s % 8)
+        return fail(INDEXER_EINVAL, "k_stride_s=%lld must be >= head_dim and a multiple of 8", (long long)k_stride_s);
+    const int64_t need_blocks = ((int64_t)max_seq_len + block_size - 1) / block_size;
+    if (bt_stride < need_blocks)
+        return fail(INDEXER_EINVAL, "bt_stride=%lld < ceil(max_seq_len/block_size)=%lld", (long long)bt_stride,
+                    (long long)need_blocks);
+    if (mask) {
+        if (!aligned(mask, 2)) return fail(INDEXER_EINVAL, "mask must be 2-byte aligned");
+        if (mask_stride_t < max_seq_len)
+            return fail(INDEXER_EINVAL, "mask_stride_t=%lld < max_seq_len=%d", (long long)mask_stride_t, max_seq_len);
+    }
+    return INDEXER_OK;
+}
+
+indexer_status check_score_out(const float *score, int64_t score_stride_t, int32_t n_cols) {
+    if (!score) return fail(INDEXER_EINVAL, "score is NULL");
+    if (!aligned(score, 4)) return fail(INDEXER_EINVAL, "score must be 4-byte aligned");
+    if (score_stride_t < n_cols)
+        return fail(INDEXER_EINVAL, "score_stride_t=%lld < row width %d", (long long)score_stride_t, n_cols);
+    return INDEXER_OK;
+}
+
+indexer_status check_topk_out(int32_t k_top, const int32_t *idx, const float *val, int64_t out_stride) {
+    if (k_top < 1) return fail(INDEXER_EINVAL, "k_top=%d must be >= 1", k_top);
+    if (k_top > INDEXER_MAX_K_TOP)
+        return fail(INDEXER_ENOTSUP, "k_top=%d exceeds INDEXER_MAX_K_TOP=%d", k_top, INDEXER_MAX_K_TOP);
+    if (!idx) return fail(INDEXER_EINVAL, "idx is NULL");
+    if (!aligned(idx, 4) || (val && !aligned(val, 4)))
+        return fail(INDEXER_EINVAL, "idx and val must be 4-byte aligned");
+    if (out_stride < k_top)
+        return fail(INDEXER_EINVAL, "out_stride=%lld < k_top=%d", (long long)out_stride, k_top);
+    return INDEXER_OK;
+}
+
+size_t fused_bytes(int32_t n_rows, int32_t n_cols, int32_t k_top) {
+    const size_t row = round_up((size_t)n_cols, 4) * 4;
+    return round_up(row * (size_t)n_rows, 256) + round_up(lidx::topk_workspace_bytes(n_rows, n_cols, k_top), 256);
+}
+
+lidx::ScoreArgs prefill_args(const void *q, int64_t q_stride_t, int64_t q_stride_h, const void *k,
+                             int64_t k_stride_s, const float *w, const void *mask, int64_t mask_stride_t,
+                             const int32_t *vis_len, int32_t n_tokens, int32_t n_pool, float *score,
+                             int64_t score_stride_t) {
+    lidx::ScoreArgs a{};
+    a.q = (const _Float16 *)q;
+    a.q_st = q_stride_t;
+    a.q_sh = q_stride_h;
+    a.k = (const _Float16 *)k;
+    a.k_ss = k_stride_s;
+    a.block_size = 1;
+    a.bs_shift = 0;
+    a.w = w;
+    a.mask = (const _Float16 *)mask;
+    a.mask_st = mask_stride_t;
+    a.vis_len = vis_len;
+    a.score = score;
+    a.score_st = score_stride_t;
+    a.n_rows = n_tokens;
+    a.n_cols = n_pool;
+    a.q_per_req = n_tokens;
+    a.mask_vec = mask && aligned(mask, 16) && mask_stride_t % 8 == 0;
+    a.score_vec = aligned(score, 16) && score_stride_t % 4 == 0;
+    return a;
+}
+
+lidx::ScoreArgs decode_args(const void *q, int64_t q_stride_t, int64_t q_stride_h, const void *k_cache,
+                            int32_t block_size, int64_t k_stride_s, const int32_t *block_table,
+                            int64_t bt_stride, const int32_t *seq_lens, int32_t n_requests, int32_t query_len,
+                            int32_t max_seq_len, const float *w, const void *mask, int64_t mask_stride_t,
+                            float *score, int64_t score_stride_t) {
+    lidx::ScoreArgs a{};
+    a.q = (const _Float16 *)q;
+    a.q_st = q_stride_t;
+    a.q_sh = q_stride_h;
+    a.k = (const _Float16 *)k_cache;
+    a.k_ss = k_stride_s;
+    a.block_table = block_table;
+    a.bt_stride = bt_stride;
+    a.block_size = block_size;
+    a.bs_shift = log2_exact(block_size);
+    a.seq_lens = seq_lens;
+    a.w = w;
+    a.mask = (const _Float16 *)mask;
+    a.mask_st = mask_stride_t;
+    a.score = score;
+    a.score_st = score_stride_t;
+    a.n_rows = n_requests * query_len;
+    a.n_cols = max_seq_len;
+    a.q_per_req = query_len;
+    a.mask_vec = mask && aligned(mask, 16) && mask_stride_t % 8 == 0;
+    a.score_vec = aligned(score, 16) && score_stride_t % 4 == 0;
+    return a;
+}
+
+indexer_status run_score(lidx::ScoreArgs &a, int n_heads, int head_dim, bool paged, int n_requests,
+                         hipStream_t stream) {
+    lidx::ScorePlan p = lidx::plan_score(a, n_heads, head_dim, paged, n_requests);
+    if ((int64_t)a.n_row_groups * a.n_chunks > INT32_MAX)
+        return fail(INDEXER_EINVAL, "problem too large for one launch");
+    return hip_status(lidx::launch_score(a, p, n_heads, head_dim, paged, stream), "score kernel launch");
+}
+
+indexer_status run_topk(const float *score, int64_t score_stride_t, int32_t n_rows, int32_t n_cols,
+                        const int32_t *row_len, int32_t k_top, int32_t *idx, float *val, int64_t out_stride,
+                        void *workspace, hipStream_t stream) {
+    lidx::TopkArgs t{};
+    t.score = score;
+    t.score_st = score_stride_t;
+    t.n_rows = n_rows;
+    t.n_cols = n_cols;
+    t.row_len = row_len;
+    t.k_top = k_top;
+    t.idx = idx;
+    t.val = val;
+    t.out_st = out_stride;
+    return hip_status(lidx::launch_topk(t, workspace, stream), "top-k kernel launch");
+}
+
+}  // namespace
+
+namespace lidx {
+
+int device_cu_count() {
+    static std::mutex mu;
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    std::lock_guard<std::mutex> lock(mu);
+    if (cached[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) v = 256;
+        cached[dev] = v;
+    }
+    return cached[dev];
+}
+
+}  // namespace lidx
+
+extern "C" {
+
+int indexer_abi_version(void) { return INDEXER_ABI_VERSION; }
+
+const char *indexer_status_string(int status) {
+    switch (status) {
+        case INDEXER_OK: return "INDEXER_OK";
+        case INDEXER_EINVAL: return "INDEXER_EINVAL: invalid argument";
+        case INDEXER_ENOTSUP: return "INDEXER_ENOTSUP: unsupported shape";
+        case INDEXER_EWORKSPACE: return "INDEXER_EWORKSPACE: workspace too small";
+        case INDEXER_EHIP: return "INDEXER_EHIP: HIP runtime error";
+        default: return "unknown indexer status";
+    }
+}
+
+const char *indexer_last_error(void) { return g_last_error; }
+
+size_t indexer_workspace_bytes(int op, int32_t n_rows, int32_t n_cols, int32_t k_top) {
+    if (n_rows < 0 || n_cols < 0 || k_top < 0) return (size_t)-1;
+    switch (op) {
+        case INDEXER_OP_TOPK: return lidx::topk_workspace_bytes(n_rows, n_cols, k_top);
+        case INDEXER_OP_FUSED_PREFILL:
+        case INDEXER_OP_FUSED_DECODE: return fused_bytes(n_rows, n_cols, k_top);
+        default: return (size_t)-1;
+    }
+}
+
+indexer_status indexer_score_prefill(const void *q, int64_t q_stride_t, int64_t q_stride_h, const void *k,
+                                     int64_t k_stride_s, const float *w, const void *mask, int64_t mask_stride_t,
+                                     const int32_t *vis_len, int32_t n_tokens, int32_t n_pool, int32_t n_heads,
+                                     int32_t head_dim, float *score, int64_t score_stride_t, void *stream) {
+    indexer_status st = check_prefill(q, q_stride_t, q_stride_h, k, k_stride_s, w, mask, mask_stride_t, vis_len,
+                                      n_tokens, n_pool, n_heads, head_dim);
+    if (st != INDEXER_OK) return st;
+    if ((st = check_score_out(score, score_stride_t, n_pool)) != INDEXER_OK) return st;
+    if (n_tokens == 0 || n_pool == 0) return ok();
+    lidx::ScoreArgs a = prefill_args(q, q_stride_t, q_stride_h, k, k_stride_s, w, mask, mask_stride_t, vis_len,
+                                     n_tokens, n_pool, score, score_stride_t);
+    return run_score(a, n_heads, head_dim, false, 1, (hipStream_t)stream);
+}
+
+indexer_status indexer_score_decode(const void *q, int64_t q_stride_t, int64_t q_stride_h, const void *k_cache,
+                                    int32_t block_size, int64_t k_stride_s, const int32_t *block_table,
+                                    int64_t bt_stride, const int32_t *seq_lens, int32_t n_requests,
+                                    int32_t query_len, int32_t max_seq_len, const float *w, const void *mask,
+                                    int64_t mask_stride_t, int32_t n_heads, int32_t head_dim, float *score,
+                                    int64_t score_stride_t, void *stream) {
+    indexer_status st = check_decode(q, q_stride_t, q_stride_h, k_cache, block_size, k_stride_s, block_table,
+                                     bt_stride, seq_lens, n_requests, query_len, max_seq_len, w, mask,
+                                     mask_stride_t, n_heads, head_dim);
+    if (st != INDEXER_OK) return st;
+    if ((st = check_score_out(score, score_stride_t, max_seq_len)) != INDEXER_OK) return st;
+    if (n_requests == 0 || max_seq_len == 0) return ok();
+    lidx::ScoreArgs a = decode_args(q, q_stride_t, q_stride_h, k_cache, block_size, k_stride_s, block_table,
+                                    bt_stride, seq_lens, n_requests, query_len, max_seq_len, w, mask,
+                                    mask_stride_t, score, score_stride_t);
+    return run_score(a, n_heads, head_dim, true, n_requests, (hipStream_t)stream);
+}
+
+indexer_status indexer_topk(const float *score, int64_t score_stride_t, int32_t n_rows, int32_t n_cols,
+                            const int32_t *row_len, int32_t k_top, int32_t *idx, float *val, int64_t out_stride,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    if (n_rows < 0 || n_cols < 0) return fail(INDEXER_EINVAL, "n_rows=%d n_cols=%d must be >= 0", n_rows, n_cols);
+    indexer_status st = check_topk_out(k_top, idx, val, out_stride);
+    if (st != INDEXER_OK) return st;
+    if (n_rows > 0 && n_cols > 0 && (st = check_score_out(score, score_stride_t, n_cols)) != INDEXER_OK) return st;
+    if (row_len && !aligned(row_len, 4)) return fail(INDEXER_EINVAL, "row_len must be 4-byte aligned");
+    const size_t need = lidx::topk_workspace_bytes(n_rows, n_cols, k_top);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(INDEXER_EWORKSPACE, "top-k needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    if (n_rows == 0) return ok();
+    return run_topk(score, score_stride_t, n_rows, n_cols, row_len, k_top, idx, val, out_stride, workspace,
+                    (hipStream_t)stream);
+}
+
+indexer_status indexer_score_topk_fused_prefill(const void *q, int64_t q_stride_t, int64_t q_stride_h,
+                                                const void *k, int64_t k_stride_s, const float *w,
+                                                const void *mask, int64_t mask_stride_t, const int32_t *vis_len,
+                                                int32_t n_tokens, int32_t n_pool, int32_t n_heads,
+                                                int32_t head_dim, int32_t k_top, int32_t *idx, float *val,
+                                                int64_t out_stride, void *workspace, size_t workspace_bytes,
+                                                void *stream) {
+    indexer_status st = check_prefill(q, q_stride_t, q_stride_h, k, k_stride_s, w, mask, mask_stride_t, vis_len,
+                                      n_tokens, n_pool, n_heads, head_dim);
+    if (st != INDEXER_OK) return st;
+    if ((st = check_topk_out(k_top, idx, val, out_stride)) != INDEXER_OK) return st;
+    const size_t need = fused_bytes(n_tokens, n_pool, k_top);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(INDEXER_EWORKSPACE, "fused prefill needs %zu bytes of 256-byte aligned workspace, got %zu", need,
+                    workspace ? workspace_bytes : 0);
+    if (n_tokens == 0) return ok();
+    const int64_t row = (int64_t)round_up((size_t)n_pool, 4);
+    float *scores = (float *)workspace;
+    void *topk_ws = (char *)workspace + round_up((size_t)row * 4 * n_tokens, 256);
+    hipStream_t s = (hipStream_t)stream;
+    if (n_pool > 0) {
+        lidx::ScoreArgs a = prefill_args(q, q_stride_t, q_stride_h, k, k_stride_s, w, mask, mask_stride_t, vis_len,
+                                         n_tokens, n_pool, scores, row);
+        if ((st = run_score(a, n_heads, head_dim, false, 1, s)) != INDEXER_OK) return st;
+    }
+    return run_topk(scores, row, n_tokens, n_pool, nullptr, k_top, idx, val, out_stride, topk_ws, s);
+}
+
+indexer_status indexer_score_topk_fused_decode(const void *q, int64_t q_stride_t, int64_t q_stride_h,
+                                               const void *k_cache, int32_t block_size, int64_t k_stride_s,
+                                               const int32_t *block_table, int64_t bt_stride,
+                                               const int32_t *seq_lens, int32_t n_requests, int32_t query_len,
+                                               int32_t max_seq_len, const float *w, const void *mask,
+                                               int64_t mask_stride_t, int32_t n_heads, int32_t head_dim,
+                                               int32_t k_top, int32_t *idx, float *val, int64_t out_stride,
+                                               void *workspace, size_t workspace_bytes, void *stream) {
+    indexer_status st = check_decode(q, q_stride_t, q_stride_h, k_cache, block_size, k_stride_s, block_table,
+                                     bt_stride, seq_lens, n_requests, query_len, max_seq_len, w, mask,
+                                     mask_stride_t, n_heads, head_dim);
+    if (st != INDEXER_OK) return st;
+    if ((st = check_topk_out(k_top, idx, val, out_stride)) != INDEXER_OK) return st;
+    const int32_t n_rows = n_requests * query_len;
+    const size_t need = fused_bytes(n_rows, max_seq_len, k_top);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(INDEXER_EWORKSPACE, "fused decode needs %zu bytes of 256-byte aligned workspace, got %zu", need,
+                    workspace ? workspace_bytes : 0);
+    if (n_rows == 0) return ok();
+    const int64_t row = (int64_t)round_up((size_t)max_seq_len, 4);
+    float *scores = (float *)workspace;
+    void *topk_ws = (char *)workspace + round_up((size_t)row * 4 * n_rows, 256);
+    hipStream_t s = (hipStream_t)stream;
+    if (max_seq_len > 0) {
+        lidx::ScoreArgs a = decode_args(q, q_stride_t, q_stride_h, k_cache, block_size, k_stride_s, block_table,
+                                        bt_stride, seq_lens, n_requests, query_len, max_seq_len, w, mask,
+                                        mask_stride_t, scores, row);
+        if ((st = run_score(a, n_heads, head_dim, true, n_requests, s)) != INDEXER_OK) return st;
+    }
+    return run_topk(scores, row, n_rows, max_seq_len, nullptr, k_top, idx, val, out_stride, topk_ws, s);
+}
+
+}  // extern "C"

@@ -1,0 +1,497 @@
+// Lightning-indexer score kernel for gfx950 (CDNA4).
+//
+//   score[t][s] = sum_h w[h] * max(q[t][h][:] . k[s][:], 0) + mask[t][s]
+//
+// (llama.cpp b11372: every head's product is rectified and summed in place
+// into one [n_pool, n_tokens] score, keys read once for all heads, f16 pool
+// mask; vLLM PR #45743: decode batches all query tokens of a request into
+// one matrix product and uses no implicit scale.)
+//
+// Design
+// ------
+// The per-key work is a dense contraction: for a group of query rows the
+// [rows*heads, d] x [d, keys] product feeds a rectify/weight/head-sum
+// epilogue.  It runs on v_mfma_f32_32x32x16_f16 with fp32 accumulation.
+//
+//  * A workgroup (4 waves) owns a few query rows and a range of keys.  Each
+//    wave keeps its rows' q fragments (all heads) in registers for the whole
+//    key loop, so q is read once per workgroup.
+//  * Key tiles are streamed global -> LDS with gfx950's direct-to-LDS 16-byte
+//    loads, double buffered, into an XOR-swizzled layout that makes the
+//    per-lane 16-byte fragment reads bank-conflict free.  Every key tile is
+//    read from LDS by every wave, i.e. once for all heads and all rows of the
+//    workgroup.
+//  * M-block row mapping: the 32 rows of one MFMA block are 16/8/4 heads of
+//    2/4/8 query rows, arranged so that accumulator register r of a lane
+//    always holds the same head.  The head weight is then a wave-uniform
+//    (scalar) operand, and the sum over heads stays inside each lane: no
+//    cross-lane reduction and no per-head [rows, heads, keys] tensor.
+//  * Visibility: the workgroup first bounds its key range by the rows'
+//    visible prefixes (vis_len, or seq_len - Q + 1 + j for paged decode) and,
+//    when a mask is given, by its last non -inf entry; key tiles past that
+//    bound are filled with -inf without being loaded.  A wave whose entries
+//    in a 32-key block are all invisible skips the MFMAs for that block.
+//  * Paged keys: the workgroup's block-table entries are staged in LDS once;
+//    slots past a request's length are never addressed.
+#include "internal.h"
+
+#include <math.h>
+
+namespace lidx {
+namespace {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kThreads = 256;
+constexpr int kWaves = 4;
+
+template <int H, int D>
+struct Geo {
+    static_assert(H == 4 || H == 8 || (H % 16 == 0 && H <= 64), "head count");
+    static_assert(D == 64 || D == 128, "head dim");
+    static constexpr int HPB = H < 16 ? H : 16;   // heads per M-block
+    static constexpr int TPB = 32 / HPB;          // query rows per M-block (= per wave)
+    static constexpr int MBLK = H / HPB;          // M-blocks per wave
+    static constexpr int G = HPB / 4;             // 4-register groups per row slot
+    static constexpr int SLOTS = 4 / G;           // query rows held by one lane
+    static constexpr int KSTEPS = D / 16;         // MFMA K steps
+    static constexpr int CPR = D / 8;             // 16-byte chunks per key row
+    static constexpr int ROWB = 2 * D;            // bytes per key row in LDS
+    static constexpr int ROWS_PER_256B = 256 / ROWB;
+};
+
+// Swizzled position of a key row's 16-byte chunk: the chunk index is XORed
+// with a function of the row so that the rows read by one 16-lane phase land
+// in distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ int swz(int n) {
+    return (n / Geo<4, D>::ROWS_PER_256B) & (Geo<4, D>::CPR - 1);
+}
+
+__device__ __forceinline__ bool half_is_neg_inf(_Float16 h) {
+    return __builtin_bit_cast(unsigned short, h) == 0xfc00u;
+}
+
+__device__ __forceinline__ void wait_vmem_all() {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+}
+
+// max(x, 0) as one integer max on the bit pattern: a negative float (or -0)
+// is a negative int32 and becomes +0; a non-negative float is unchanged.  One
+// v_max_i32 per accumulator (fmaxf would add a NaN-quieting v_max first).
+// Inline asm is avoided here on purpose: the hazard checks between MFMA
+// results and their VALU readers only see compiler-visible instructions.
+__device__ __forceinline__ float relu(float x) {
+    return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
+}
+
+// Per-head weights are read through the constant address space so that they
+// load with scalar instructions and feed the epilogue FMAs as SGPR operands.
+typedef const __attribute__((address_space(4))) float const_f32;
+
+template <int H, int D, bool PAGED, int NBW>
+__global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
+    using G = Geo<H, D>;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+
+    const int tid = threadIdx.x;
+    const int wid = tid >> 6;
+    const int lane = tid & 63;
+    const int nc = a.nc;
+    const int tg = wid / nc;       // row group slot of this wave
+    const int col = wid - tg * nc; // key column of this wave
+    const int NK = 32 * nc * NBW;  // keys per tile
+    const int tile_bytes = NK * G::ROWB;
+    const int rows_per_wg = (kWaves / nc) * G::TPB;
+
+    // ---- the rows and keys this workgroup owns --------------------------
+    const int chunk_id = blockIdx.x % a.n_chunks;
+    // Row groups are dispatched last-first: under causal masks the later rows
+    // see more keys, so the longest workgroups start earliest.
+    const int rg = a.n_row_groups - 1 - (int)(blockIdx.x / a.n_chunks);
+    const int req = rg / a.groups_per_req;
+    const int sub = rg - req * a.groups_per_req;
+    const int req_row0 = req * a.q_per_req;
+    const int row_lo = req_row0 + sub * rows_per_wg;
+    const int row_hi = min(req_row0 + a.q_per_req, row_lo + rows_per_wg);
+    const int key_lo = chunk_id * a.chunk;
+    const int key_hi = min(a.n_cols, key_lo + a.chunk);
+
+    int seq_len = 0;
+    int key_exist = a.n_cols;  // keys that may be addressed
+    if constexpr (PAGED) {
+        seq_len = max(0, a.seq_lens[req]);
+        key_exist = min(seq_len, a.n_cols);
+    }
+    auto row_vis = [&](int t) -> int {
+        if constexpr (PAGED) {
+            const int j = t - req_row0;
+            return min(max(seq_len - a.q_per_req + 1 + j, 0), a.n_cols);
+        } else {
+            return a.vis_len ? min(max(a.vis_len[t], 0), a.n_cols) : a.n_cols;
+        }
+    };
+
+    int *misc = reinterpret_cast<int *>(smem + 2 * tile_bytes);
+    int *bt_lds = misc + 4;
+
+    // ---- bound the key range: prefix lengths, then the mask ------------
+    if (tid == 0) {
+        misc[0] = key_lo;
+        misc[1] = key_lo;
+    }
+    __syncthreads();
+    if (tid < row_hi - row_lo) atomicMax(&misc[0], min(row_vis(row_lo + tid), key_hi));
+    __syncthreads();
+    int bound = misc[0];  // no row of this workgroup sees a key >= bound
+
+    if (a.mask != nullptr && bound > key_lo) {
+        int last = key_lo;  // 1 + the last visible key seen by this thread
+        const int nrows = row_hi - row_lo;
+        const int span = bound - key_lo;
+        const int nch = (span + 7) >> 3;
+        for (int c = tid; c < nrows * nch; c += kThreads) {
+            const int r = c / nch;
+            const int s = key_lo + (c - r * nch) * 8;
+            const int t = row_lo + r;
+            const int rv = min(row_vis(t), bound);
+            if (s >= rv) continue;
+            const _Float16 *mrow = a.mask + (int64_t)t * a.mask_st;
+            if (a.mask_vec && s + 8 <= a.n_cols) {
+                const uint4 v = *reinterpret_cast<const uint4 *>(mrow + s);
+                const unsigned int wv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+                for (int e = 7; e >= 0; --e) {
+                    const unsigned int hbits = (wv[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+                    if (s + e < rv && hbits != 0xfc00u) {
+                        last = max(last, s + e + 1);
+                        break;
+                    }
+                }
+            } else {
+                for (int e = min(8, rv - s) - 1; e >= 0; --e) {
+                    if (!half_is_neg_inf(mrow[s + e])) {
+                        last = max(last, s + e + 1);
+                        break;
+                    }
+                }
+            }
+        }
+        if (last > key_lo) atomicMax(&misc[1], last);
+        __syncthreads();
+        bound = misc[1];
+    }
+
+    const int load_limit = min(bound, key_exist);
+    int b_lo = 0;
+    if constexpr (PAGED) {
+        // stage the block ids of the keys this workgroup will load
+        const int bs = a.block_size;
+        b_lo = key_lo / bs;
+        const int b_hi = load_limit > key_lo ? (load_limit + bs - 1) / bs : b_lo;
+        for (int i = tid; i < b_hi - b_lo; i += kThreads)
+            bt_lds[i] = a.block_table[(int64_t)req * a.bt_stride + b_lo + i];
+        __syncthreads();
+    }
+
+    const int n_tiles = bound > key_lo ? (bound - key_lo + NK - 1) / NK : 0;
+
+    // ---- q fragments (A operand) for this wave's rows -------------------
+    const int m = lane & 31;
+    const int kh = lane >> 5;
+    const int tok_m = (((m >> 3) / G::G) << 1) + ((m >> 2) & 1);
+    const int head_m = ((m >> 3) % G::G) * 4 + (m & 3);
+    const int wave_row0 = row_lo + tg * G::TPB;
+    half8 qa[G::MBLK][G::KSTEPS];
+    {
+        const int t = wave_row0 + tok_m;
+        const bool ok = t < row_hi && n_tiles > 0;
+#pragma unroll
+        for (int mb = 0; mb < G::MBLK; ++mb) {
+            const _Float16 *src = a.q + (int64_t)t * a.q_st +
+                                  (int64_t)(mb * G::HPB + head_m) * a.q_sh + kh * (D / 2);
+#pragma unroll
+            for (int kk = 0; kk < G::KSTEPS; ++kk) {
+                if (ok) {
+                    qa[mb][kk] = *reinterpret_cast<const half8 *>(src + kk * 8);
+                } else {
+                    qa[mb][kk] = half8{};
+                }
+            }
+        }
+    }
+
+    const_f32 *wc = (const_f32 *)a.w;
+
+    // rows this lane writes, and their visible prefixes
+    int out_t[G::SLOTS];
+    int out_vis[G::SLOTS];
+#pragma unroll
+    for (int j = 0; j < G::SLOTS; ++j) {
+        out_t[j] = wave_row0 + 2 * j + kh;
+        out_vis[j] = out_t[j] < row_hi ? row_vis(out_t[j]) : 0;
+    }
+
+    auto key_src = [&](int s) -> const _Float16 * {
+        if constexpr (PAGED) {
+            int blk, slot;
+            if (a.bs_shift >= 0) {
+                blk = s >> a.bs_shift;
+                slot = s - (blk << a.bs_shift);
+            } else {
+                blk = s / a.block_size;
+                slot = s - blk * a.block_size;
+            }
+            const int64_t phys = bt_lds[blk - b_lo];
+            return a.k + (phys * a.block_size + slot) * a.k_ss;
+        } else {
+            return a.k + (int64_t)s * a.k_ss;
+        }
+    };
+
+    auto issue_tile = [&](int tile, int buf) {
+        const int s0 = key_lo + tile * NK;
+        unsigned char *base = smem + buf * tile_bytes;
+        const int n_iter = (NK * G::CPR) / kThreads;
+        for (int it = 0; it < n_iter; ++it) {
+            const int c = (it * kWaves + wid) * 64 + lane;
+            const int n = c / G::CPR;
+            const int lc = (c & (G::CPR - 1)) ^ swz<D>(n);
+            const int s = s0 + n;
+            const _Float16 *src = s < load_limit ? key_src(s) + lc * 8 : a.k;
+            __builtin_amdgcn_global_load_lds(
+                src, (__attribute__((address_space(3))) void *)(base + (it * kWaves + wid) * 1024),
+                16, 0, 0);
+        }
+    };
+
+    _Float16 mnext[NBW][G::SLOTS];
+    auto load_mask = [&](int tile) {
+        const int s0 = key_lo + tile * NK;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+            const int s = s0 + (col * NBW + nb) * 32 + m;
+#pragma unroll
+            for (int j = 0; j < G::SLOTS; ++j) {
+                _Float16 v = (_Float16)0.0f;
+                if (a.mask != nullptr && s < out_vis[j]) v = a.mask[(int64_t)out_t[j] * a.mask_st + s];
+                mnext[nb][j] = v;
+            }
+        }
+    };
+
+    // results of the previous tile, stored after the next tile's loads are
+    // issued so that their write latency overlaps the following compute
+    float pend[NBW][G::SLOTS];
+    int pend_s = -1;
+    auto flush = [&]() {
+        if (pend_s < 0) return;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+            const int s = pend_s + nb * 32;
+            if (s < key_hi) {
+#pragma unroll
+                for (int j = 0; j < G::SLOTS; ++j)
+                    if (out_t[j] < row_hi) a.score[(int64_t)out_t[j] * a.score_st + s] = pend[nb][j];
+            }
+        }
+    };
+
+    if (n_tiles > 0) {
+        load_mask(0);
+        issue_tile(0, 0);
+    }
+    for (int i = 0; i < n_tiles; ++i) {
+        wait_vmem_all();
+        __syncthreads();  // tile i is in LDS; every wave is done with tile i-1
+        _Float16 mcur[NBW][G::SLOTS];
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb)
+#pragma unroll
+            for (int j = 0; j < G::SLOTS; ++j) mcur[nb][j] = mnext[nb][j];
+        if (i + 1 < n_tiles) {
+            load_mask(i + 1);
+            issue_tile(i + 1, (i + 1) & 1);
+        }
+        flush();
+
+        const unsigned char *buf = smem + (i & 1) * tile_bytes;
+        const int s0 = key_lo + i * NK;
+#pragma unroll
+        for (int nb = 0; nb < NBW; ++nb) {
+            const int nloc = (col * NBW + nb) * 32;
+            const int s = s0 + nloc + m;
+            bool vis[G::SLOTS];
+            bool any = false;
+#pragma unroll
+            for (int j = 0; j < G::SLOTS; ++j) {
+                vis[j] = s < out_vis[j] && !half_is_neg_inf(mcur[nb][j]);
+                any |= vis[j];
+            }
+            float res[G::SLOTS];
+#pragma unroll
+            for (int j = 0; j < G::SLOTS; ++j) res[j] = -INFINITY;
+            if (__builtin_amdgcn_ballot_w64(any) != 0) {
+                f32x16 acc[G::MBLK];
+#pragma unroll
+                for (int mb = 0; mb < G::MBLK; ++mb) acc[mb] = f32x16{};
+                const int n = nloc + m;
+                const unsigned char *rowp = buf + n * G::ROWB;
+                const int f = swz<D>(n);
+                auto bfrag = [&](int kk) {
+                    return *reinterpret_cast<const half8 *>(rowp + (((kh * G::KSTEPS + kk) ^ f) << 4));
+                };
+                half8 b = bfrag(0);
+#pragma unroll
+                for (int kk = 0; kk < G::KSTEPS; ++kk) {
+                    // fetch the next K step's key fragment while these MFMAs run
+                    const half8 bn = kk + 1 < G::KSTEPS ? bfrag(kk + 1) : b;
+#pragma unroll
+                    for (int mb = 0; mb < G::MBLK; ++mb)
+                        acc[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[mb][kk], b, acc[mb], 0, 0, 0);
+                    b = bn;
+                }
+                // epilogue: register r of M-block mb is head mb*HPB + r % (4G)
+                // of row slot r / (4G); rectify, weight, sum over heads
+#pragma unroll
+                for (int j = 0; j < G::SLOTS; ++j) {
+                    float sum = 0.0f;
+#pragma unroll
+                    for (int mb = 0; mb < G::MBLK; ++mb)
+#pragma unroll
+                        for (int rr = 0; rr < 4 * G::G; ++rr)
+                            sum = fmaf(relu(acc[mb][4 * G::G * j + rr]),
+                                       wc[mb * G::HPB + rr], sum);
+                    if (vis[j]) res[j] = sum + (float)mcur[nb][j];
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < G::SLOTS; ++j) pend[nb][j] = res[j];
+        }
+        pend_s = s0 + col * NBW * 32 + m;
+    }
+    flush();
+
+    // ---- keys past the bound: -inf without loading anything ------------
+    const int fill_lo = min(key_lo + n_tiles * NK, key_hi);
+    if (fill_lo < key_hi) {
+        const int nrows = row_hi - row_lo;
+        const int width = key_hi - fill_lo;
+        if (a.score_vec && (fill_lo & 3) == 0) {
+            const int w4 = width >> 2;
+            const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            for (int c = tid; c < nrows * w4; c += kThreads) {
+                const int r = c / w4;
+                const int i4 = c - r * w4;
+                *reinterpret_cast<float4 *>(a.score + (int64_t)(row_lo + r) * a.score_st + fill_lo + 4 * i4) = ninf;
+            }
+            const int tail = width & 3;
+            for (int c = tid; c < nrows * tail; c += kThreads) {
+                const int r = c / tail;
+                a.score[(int64_t)(row_lo + r) * a.score_st + fill_lo + 4 * w4 + (c - r * tail)] = -INFINITY;
+            }
+        } else {
+            for (int c = tid; c < nrows * width; c += kThreads) {
+                const int r = c / width;
+                a.score[(int64_t)(row_lo + r) * a.score_st + fill_lo + (c - r * width)] = -INFINITY;
+            }
+        }
+    }
+}
+
+// Dynamic LDS above 64 KiB must be enabled per kernel; done once per
+// instantiation for the largest size used so far.
+template <typename K>
+hipError_t allow_lds(K kern, size_t bytes) {
+    static int allowed = 65536;
+    if ((int)bytes <= allowed) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute((const void *)kern,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) allowed = (int)bytes;
+    return e;
+}
+
+template <int H, int D, bool PAGED>
+hipError_t launch_hd(const ScoreArgs &a, const ScorePlan &p, hipStream_t stream) {
+    if (p.nbw == 2) {
+        auto kern = score_kernel<H, D, PAGED, 2>;
+        hipError_t e = allow_lds(kern, p.lds_bytes);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, p.grid, dim3(kThreads), p.lds_bytes, stream, a);
+    } else {
+        auto kern = score_kernel<H, D, PAGED, 1>;
+        hipError_t e = allow_lds(kern, p.lds_bytes);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(kern, p.grid, dim3(kThreads), p.lds_bytes, stream, a);
+    }
+    return hipGetLastError();
+}
+
+template <int H, bool PAGED>
+hipError_t launch_h(const ScoreArgs &a, const ScorePlan &p, int D, hipStream_t stream) {
+    return D == 64 ? launch_hd<H, 64, PAGED>(a, p, stream) : launch_hd<H, 128, PAGED>(a, p, stream);
+}
+
+template <bool PAGED>
+hipError_t launch_paged(const ScoreArgs &a, const ScorePlan &p, int H, int D, hipStream_t stream) {
+    switch (H) {
+        case 4: return launch_h<4, PAGED>(a, p, D, stream);
+        case 8: return launch_h<8, PAGED>(a, p, D, stream);
+        case 16: return launch_h<16, PAGED>(a, p, D, stream);
+        case 32: return launch_h<32, PAGED>(a, p, D, stream);
+        default: return launch_h<64, PAGED>(a, p, D, stream);
+    }
+}
+
+}  // namespace
+
+bool score_shape_supported(int n_heads, int head_dim) {
+    const bool h_ok = n_heads == 4 || n_heads == 8 || n_heads == 16 || n_heads == 32 || n_heads == 64;
+    const bool d_ok = head_dim == 64 || head_dim == 128;
+    return h_ok && d_ok;
+}
+
+ScorePlan plan_score(ScoreArgs &a, int n_heads, int head_dim, bool paged, int n_requests) {
+    ScorePlan p{};
+    const int hpb = n_heads < 16 ? n_heads : 16;
+    const int tpb = 32 / hpb;
+    // waves along rows: enough row groups for the rows one request owns
+    const int rows = a.q_per_req;
+    int ng = 1;
+    while (ng < kWaves && ng * tpb < rows) ng *= 2;
+    p.nc = kWaves / ng;
+    p.nbw = p.nc == 1 ? 2 : 1;
+    p.tile_keys = 32 * p.nc * p.nbw;
+    p.rows_per_group = ng * tpb;
+    a.nc = p.nc;
+    a.groups_per_req = rows > 0 ? (rows + p.rows_per_group - 1) / p.rows_per_group : 0;
+    a.n_row_groups = a.groups_per_req * (paged ? n_requests : 1);
+
+    // keys per workgroup: aim for a few workgroups per compute unit
+    const int cus = device_cu_count();
+    const int target = 4 * cus;
+    const int max_tiles = (a.n_cols + p.tile_keys - 1) / p.tile_keys;
+    int n_chunks = a.n_row_groups > 0 ? (target + a.n_row_groups - 1) / a.n_row_groups : 1;
+    n_chunks = n_chunks < 1 ? 1 : (n_chunks > max_tiles ? max_tiles : n_chunks);
+    if (n_chunks < 1) n_chunks = 1;
+    const int tiles_per_chunk = (max_tiles + n_chunks - 1) / n_chunks;
+    a.chunk = (tiles_per_chunk > 0 ? tiles_per_chunk : 1) * p.tile_keys;
+    a.n_chunks = (a.n_cols + a.chunk - 1) / a.chunk;
+    if (a.n_chunks < 1) a.n_chunks = 1;
+
+    const size_t tile_bytes = (size_t)p.tile_keys * 2 * head_dim;
+    size_t bt_entries = 0;
+    if (paged) bt_entries = (size_t)(a.chunk + a.block_size - 1) / a.block_size + 2;
+    p.lds_bytes = 2 * tile_bytes + 16 + 4 * bt_entries;
+    p.grid = dim3((unsigned)(a.n_row_groups * a.n_chunks));
+    return p;
+}
+
+hipError_t launch_score(const ScoreArgs &a, const ScorePlan &p, int n_heads, int head_dim,
+                        bool paged, hipStream_t stream) {
+    if (paged) return launch_paged<true>(a, p, n_heads, head_dim, stream);
+    return launch_paged<false>(a, p, n_heads, head_dim, stream);
+}
+
+}  // namespace lidx

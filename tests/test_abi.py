@@ -1,0 +1,154 @@
+"""The C-ABI library on the host: it loads without a GPU, exports every
+symbol include/indexer.h declares, and rejects bad arguments before it would
+enqueue anything (none of these calls reaches a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import sparse_attention_lightning_indexer_amd as li
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "indexer.h")
+
+A = 0x10000        # a fake, 256-byte aligned "device" address; never dereferenced
+B = 0x20000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(indexer_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return li.load_library()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert len(names) == 9, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(li.EXPORTS)
+
+
+def test_version_and_status_strings(lib):
+    v = int(re.search(r"#define INDEXER_ABI_VERSION (\d+)", open(HEADER).read()).group(1))
+    assert lib.indexer_abi_version() == v
+    assert lib.indexer_status_string(0) == b"INDEXER_OK"
+    for s in range(1, 5):
+        assert lib.indexer_status_string(s).startswith(b"INDEXER_E")
+    assert lib.indexer_status_string(99) == b"unknown indexer status"
+
+
+def test_workspace_bytes(lib):
+    assert lib.indexer_workspace_bytes(li.OP_TOPK, 10, 100, 8) == 0
+    # fused: scores [rows][round_up(cols, 4)] f32, rounded up to 256 bytes
+    assert lib.indexer_workspace_bytes(li.OP_FUSED_PREFILL, 3, 5, 2) == 256
+    assert lib.indexer_workspace_bytes(li.OP_FUSED_PREFILL, 8192, 8192, 2048) == 8192 * 8192 * 4
+    assert lib.indexer_workspace_bytes(li.OP_FUSED_DECODE, 128, 16383, 2048) == 128 * 16384 * 4
+    assert lib.indexer_workspace_bytes(7, 1, 1, 1) == ctypes.c_size_t(-1).value
+    assert lib.indexer_workspace_bytes(li.OP_TOPK, -1, 1, 1) == ctypes.c_size_t(-1).value
+
+
+def prefill(lib, **kw):
+    a = dict(q=A, qst=64 * 128, qsh=128, k=B, kss=128, w=A, mask=None, mst=0, vis=None,
+             T=4, P=16, H=64, d=128, score=A, sst=16, stream=None)
+    a.update(kw)
+    return lib.indexer_score_prefill(a["q"], a["qst"], a["qsh"], a["k"], a["kss"], a["w"], a["mask"],
+                                     a["mst"], a["vis"], a["T"], a["P"], a["H"], a["d"], a["score"],
+                                     a["sst"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(H=12), li.ENOTSUP, b"n_heads=12"),
+    (dict(H=128), li.ENOTSUP, b"not supported"),
+    (dict(d=96, qsh=96, qst=96 * 64, kss=96), li.ENOTSUP, b"head_dim=96"),
+    (dict(q=None), li.EINVAL, b"q is NULL"),
+    (dict(k=None), li.EINVAL, b"k is NULL"),
+    (dict(w=None), li.EINVAL, b"w is NULL"),
+    (dict(score=None), li.EINVAL, b"score is NULL"),
+    (dict(q=A + 2), li.EINVAL, b"q must be 16-byte aligned"),
+    (dict(k=B + 8), li.EINVAL, b"k must be 16-byte aligned"),
+    (dict(qsh=100), li.EINVAL, b"q_stride_h"),
+    (dict(qsh=64), li.EINVAL, b"q_stride_h"),
+    (dict(kss=120), li.EINVAL, b"k_stride_s"),
+    (dict(mask=A, mst=8), li.EINVAL, b"mask_stride_t"),
+    (dict(sst=8), li.EINVAL, b"score_stride_t"),
+    (dict(T=-1), li.EINVAL, b"n_tokens=-1"),
+])
+def test_prefill_rejects(lib, kw, status, msg):
+    assert prefill(lib, **kw) == status
+    assert msg in lib.indexer_last_error()
+
+
+def test_empty_prefill_is_a_no_op(lib):
+    assert prefill(lib, T=0) == li.OK
+    assert prefill(lib, P=0, sst=0) == li.OK
+    assert lib.indexer_last_error() == b""
+
+
+def decode(lib, **kw):
+    a = dict(q=A, qst=64 * 128, qsh=128, kc=B, bs=64, kss=128, bt=A, bts=128, sl=A, R=2, Q=4,
+             L=8192, w=A, mask=None, mst=0, H=64, d=128, score=A, sst=8192, stream=None)
+    a.update(kw)
+    return lib.indexer_score_decode(a["q"], a["qst"], a["qsh"], a["kc"], a["bs"], a["kss"], a["bt"],
+                                    a["bts"], a["sl"], a["R"], a["Q"], a["L"], a["w"], a["mask"],
+                                    a["mst"], a["H"], a["d"], a["score"], a["sst"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(bts=127), li.EINVAL, b"bt_stride"),
+    (dict(bs=0), li.EINVAL, b"block_size"),
+    (dict(Q=0), li.EINVAL, b"query_len"),
+    (dict(bt=None), li.EINVAL, b"block_table is NULL"),
+    (dict(sl=None), li.EINVAL, b"seq_lens is NULL"),
+    (dict(kc=None), li.EINVAL, b"k_cache is NULL"),
+    (dict(H=6), li.ENOTSUP, b"n_heads=6"),
+    (dict(sst=100), li.EINVAL, b"score_stride_t"),
+    (dict(R=70000, Q=70000), li.EINVAL, b"int32"),
+])
+def test_decode_rejects(lib, kw, status, msg):
+    assert decode(lib, **kw) == status
+    assert msg in lib.indexer_last_error()
+
+
+def test_empty_decode_is_a_no_op(lib):
+    assert decode(lib, R=0) == li.OK
+    assert decode(lib, L=0, sst=0, bts=0) == li.OK
+
+
+def topk(lib, **kw):
+    a = dict(score=A, sst=100, n=4, c=100, rl=None, k=8, idx=B, val=None, ost=8, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return lib.indexer_topk(a["score"], a["sst"], a["n"], a["c"], a["rl"], a["k"], a["idx"], a["val"],
+                            a["ost"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(k=0), li.EINVAL, b"k_top=0"),
+    (dict(k=4096, ost=4096), li.ENOTSUP, b"INDEXER_MAX_K_TOP"),
+    (dict(idx=None), li.EINVAL, b"idx is NULL"),
+    (dict(ost=4), li.EINVAL, b"out_stride"),
+    (dict(sst=50), li.EINVAL, b"score_stride_t"),
+    (dict(score=None), li.EINVAL, b"score is NULL"),
+    (dict(n=-2), li.EINVAL, b"n_rows=-2"),
+    (dict(idx=B + 2), li.EINVAL, b"aligned"),
+])
+def test_topk_rejects(lib, kw, status, msg):
+    assert topk(lib, **kw) == status
+    assert msg in lib.indexer_last_error()
+
+
+def test_fused_workspace_checks(lib):
+    st = lib.indexer_score_topk_fused_prefill(A, 64 * 128, 128, B, 128, A, None, 0, None, 4, 16, 64, 128,
+                                              8, B, None, 8, None, 0, None)
+    assert st == li.EWORKSPACE and b"workspace" in lib.indexer_last_error()
+    st = lib.indexer_score_topk_fused_prefill(A, 64 * 128, 128, B, 128, A, None, 0, None, 4, 16, 64, 128,
+                                              8, B, None, 8, A + 64, 1 << 20, None)
+    assert st == li.EWORKSPACE   # misaligned workspace
+    st = lib.indexer_score_topk_fused_decode(A, 64 * 128, 128, B, 64, 128, A, 2, A, 2, 1, 128, A, None, 0,
+                                             64, 128, 8, B, None, 8, A, 16, None)
+    assert st == li.EWORKSPACE

@@ -1,0 +1,245 @@
+"""GPU parity: the HIP path (through the C-ABI) against the CPU oracle on the
+same seeded inputs.  See gpu_helpers.py for the comparison bars."""
+import dataclasses
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle
+import workloads as W
+
+pytestmark = pytest.mark.gpu
+
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+import sparse_attention_lightning_indexer_amd as li  # noqa: E402
+from gpu_helpers import (DEV, check_scores, check_topk_exact, check_topk_vs_f64,  # noqa: E402
+                         denominators, dev, gpu_fused, gpu_score, gpu_topk)
+
+
+def _full_check(inp, where, check_f64_topk=True):
+    g_t = gpu_score(inp)
+    g = g_t.cpu().numpy()
+    o = oracle.score_inputs(inp)
+    den = denominators(inp)
+    err = check_scores(g, o, den, where=where)
+    gi, gv = gpu_topk(g_t, inp.k_top)
+    check_topk_exact(gi, gv, g, inp.k_top, where=where)
+    if check_f64_topk:
+        check_topk_vs_f64(gi, o, den, inp.k_top, where=where)
+    fi, fv = gpu_fused(inp)
+    assert np.array_equal(fi, gi) and np.array_equal(fv.view(np.uint32), gv.view(np.uint32)), f"{where}: fused differs"
+    return err
+
+
+# ----------------------------------------------------------------- tiny
+
+def test_tiny_reference_case():
+    inp = W.tiny()
+    err = _full_check(inp, "tiny")
+    print(f"tiny max scaled error {err:.2e}")
+
+
+# ------------------------------------------------------------ random prefill
+
+PREFILL_CASES = [
+    # T, P, H, d, k_top, mask, w, vis
+    (37, 301, 4, 64, 16, "random", "uniform", "none"),
+    (5, 96, 4, 128, 96, "none", "equal", "none"),
+    (19, 257, 8, 64, 40, "bias", "signed", "none"),
+    (33, 130, 8, 128, 7, "causal", "uniform", "random"),
+    (9, 200, 16, 64, 64, "random", "pow2", "none"),
+    (17, 513, 16, 128, 100, "zero", "signed", "random"),
+    (6, 77, 32, 64, 80, "bias", "uniform", "none"),
+    (23, 333, 32, 128, 33, "causal", "signed", "none"),
+    (3, 65, 64, 64, 5, "random", "uniform", "none"),
+    (41, 700, 64, 128, 128, "causal", "equal", "none"),
+    (11, 1000, 64, 128, 300, "none", "signed", "random"),
+    (2, 31, 64, 128, 64, "random", "uniform", "none"),
+    (8, 64, 64, 128, 2048, "causal", "uniform", "none"),
+    (4, 40, 64, 128, 8, "all_inf", "uniform", "none"),
+]
+
+
+@pytest.mark.parametrize("T,P,H,d,k_top,mask,wk,vis", PREFILL_CASES,
+                         ids=[f"T{c[0]}P{c[1]}H{c[2]}d{c[3]}k{c[4]}-{c[5]}-{c[6]}-{c[7]}" for c in PREFILL_CASES])
+def test_random_prefill(T, P, H, d, k_top, mask, wk, vis):
+    inp = W.random_prefill(1000 + T + P + H + d, T, P, H, d, k_top, mask_kind=mask, w_kind=wk, vis_kind=vis)
+    _full_check(inp, inp.name)
+
+
+@pytest.mark.parametrize("H,d", [(4, 64), (8, 128), (16, 64), (32, 128), (64, 128), (64, 64)])
+def test_integer_inputs_bit_exact(H, d):
+    """Exact-arithmetic inputs: every partial sum is representable in f32, so
+    the GPU must equal the oracle bit for bit, and so must the top-k (which
+    is full of exact ties)."""
+    inp = W.integer_prefill(77 + H + d, 29, 389, H, d, 50, mask_kind="random")
+    g_t = gpu_score(inp)
+    g = g_t.cpu().numpy()
+    o = oracle.score_inputs(inp)
+    assert np.array_equal(g.astype(np.float64), o)
+    gi, gv = gpu_topk(g_t, inp.k_top)
+    oi, ov = oracle.topk(o, inp.k_top)
+    assert np.array_equal(gi, oi)
+    assert np.array_equal(gv.astype(np.float64), ov)
+
+
+# ------------------------------------------------------------ paged decode
+
+DECODE_CASES = [
+    # R, Q, H, d, block_size, len_lo, len_hi, k_top
+    (5, 1, 64, 128, 64, 1, 300, 32),
+    (3, 4, 64, 128, 64, 3, 700, 64),
+    (4, 2, 16, 64, 16, 0, 90, 20),
+    (6, 3, 8, 128, 32, 1, 129, 50),
+    (2, 5, 64, 128, 64, 4, 260, 64),
+    (3, 8, 32, 64, 64, 8, 200, 16),
+    (2, 9, 64, 128, 64, 9, 300, 40),
+    (3, 16, 4, 64, 16, 16, 100, 10),
+    (4, 1, 64, 128, 37, 1, 250, 30),
+    (2, 4, 64, 128, 64, 0, 3, 8),
+]
+
+
+@pytest.mark.parametrize("R,Q,H,d,bs,lo,hi,k_top", DECODE_CASES,
+                         ids=[f"R{c[0]}Q{c[1]}H{c[2]}d{c[3]}bs{c[4]}L{c[5]}-{c[6]}k{c[7]}" for c in DECODE_CASES])
+def test_random_decode(R, Q, H, d, bs, lo, hi, k_top):
+    inp = W.random_decode(500 + R * Q + H + bs, R, Q, H, d, bs, lo, hi, k_top, w_kind="uniform")
+    _full_check(inp, inp.name)
+
+
+def test_decode_with_mask_and_signed_weights():
+    inp = W.random_decode(42, 4, 4, 64, 128, 64, 50, 400, 32, w_kind="signed", mask_kind="bias")
+    _full_check(inp, inp.name)
+
+
+def test_decode_wider_rows_than_lengths():
+    """max_seq_len larger than every request: the extra columns are -inf."""
+    inp = W.random_decode(43, 3, 2, 64, 128, 64, 10, 100, 16, max_seq_len=333)
+    _full_check(inp, inp.name)
+
+
+def test_paged_equals_contiguous():
+    """The same keys through a permuted block table and contiguously (query
+    j seeing the first P - T + 1 + j keys) give bit-identical scores."""
+    base = W.random_prefill(7, 4, 500, 64, 128, 16, mask_kind="none", w_kind="uniform")
+    vis = np.array([500 - 4 + 1 + j for j in range(4)], np.int32)
+    contig = dataclasses.replace(base, vis_len=vis)
+    paged = W.paged_from_prefill(base, 64)
+    a = gpu_score(contig).cpu().numpy()
+    b = gpu_score(paged).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+# ------------------------------------------------------------ metamorphic
+
+def test_weight_scaling_is_exact():
+    inp = W.random_prefill(3, 21, 450, 64, 128, 40, mask_kind="zero", w_kind="uniform")
+    a = gpu_score(inp).cpu().numpy()
+    b = gpu_score(dataclasses.replace(inp, w=(inp.w * 4).astype(np.float32))).cpu().numpy()
+    assert np.array_equal(b, a * 4)
+    ia, _ = gpu_fused(inp)
+    ib, _ = gpu_fused(dataclasses.replace(inp, w=(inp.w * 4).astype(np.float32)))
+    assert np.array_equal(ia, ib)
+
+
+def test_zero_query_gives_mask():
+    inp = W.random_prefill(4, 9, 300, 64, 128, 16, mask_kind="bias")
+    g = gpu_score(dataclasses.replace(inp, q=np.zeros_like(inp.q))).cpu().numpy()
+    assert np.array_equal(g, inp.mask.astype(np.float32))
+
+
+def test_runs_are_bit_identical():
+    inp = W.random_decode(5, 4, 4, 64, 128, 64, 100, 900, 64)
+    a = gpu_score(inp).cpu().numpy()
+    b = gpu_score(inp).cpu().numpy()
+    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+
+
+def test_heads_major_query_layout():
+    """q given as a [H, T, d] tensor viewed as [T, H, d] (strides T*d... ) is
+    read through its strides."""
+    inp = W.random_prefill(8, 12, 222, 64, 128, 16, mask_kind="random")
+    qh = torch.from_numpy(np.ascontiguousarray(inp.q.transpose(1, 0, 2))).to(DEV)
+    q_view = qh.permute(1, 0, 2)
+    g = li.score_prefill(q_view, dev(inp.k), dev(inp.w), dev(inp.mask)).cpu().numpy()
+    o = oracle.score_inputs(inp)
+    check_scores(g, o, denominators(inp), where="heads-major")
+
+
+def test_topk_row_len_and_short_rows():
+    rng = np.random.default_rng(0)
+    s = rng.integers(-20, 20, size=(50, 3000)).astype(np.float32)
+    s[rng.random(s.shape) < 0.3] = -np.inf
+    s[rng.random(s.shape) < 0.01] = np.nan
+    s[rng.random(s.shape) < 0.02] = -0.0
+    row_len = rng.integers(0, 3000, size=50).astype(np.int32)
+    for k in (1, 17, 512, 2048):
+        gi, gv = gpu_topk(dev(s), k, dev(row_len))
+        check_topk_exact(gi, gv, s, k, row_len, where=f"row_len k={k}")
+
+
+@pytest.mark.parametrize("n_cols", [1, 255, 8192, 16384, 16385, 40000, 131072])
+def test_topk_row_lengths(n_cols):
+    rng = np.random.default_rng(n_cols)
+    rows = 6
+    s = (rng.standard_normal((rows, n_cols)) * 10).astype(np.float32)
+    s[:, ::7] = np.round(s[:, ::7])          # exact ties
+    s[0, :] = 1.0                             # a row of equal scores
+    s[1, rng.random(n_cols) < 0.5] = -np.inf
+    for k in (1, 64, 2048):
+        gi, gv = gpu_topk(dev(s), k)
+        check_topk_exact(gi, gv, s, k, where=f"n_cols={n_cols} k={k}")
+
+
+# ------------------------------------------------------------ full workloads
+
+def _sampled_check(inp, rows, where):
+    g_t = gpu_score(inp)
+    g = g_t.cpu().numpy()
+    o = oracle.score_rows(inp, rows)
+    den = denominators(inp, rows)
+    err = check_scores(g[rows], o, den, where=where)
+    gi, gv = gpu_topk(g_t, inp.k_top)
+    check_topk_exact(gi, gv, g, inp.k_top, where=where)
+    check_topk_vs_f64(gi[rows], o, den, inp.k_top, where=where)
+    fi, fv = gpu_fused(inp)
+    assert np.array_equal(fi, gi), f"{where}: fused indices differ from score + top-k"
+    # masked keys are never selected; visible-count padding is exact
+    if inp.mask is not None:
+        m = inp.mask
+        sel = np.where(gi >= 0, gi, 0)
+        picked = np.take_along_axis(m, sel, axis=1)
+        assert not np.any(np.isneginf(picked.astype(np.float32)) & (gi >= 0))
+    print(f"{where}: max scaled error {err:.2e} over {len(rows)} sampled rows")
+    return g
+
+
+def test_workload_decode():
+    inp = W.decode()
+    rows = np.arange(inp.R * inp.Q)
+    _sampled_check(inp, rows, "decode")
+
+
+def test_workload_spec_decode():
+    inp = W.spec_decode()
+    rows = np.array([0, 1, 2, 3, 37, 38, 64, 127])
+    _sampled_check(inp, rows, "spec_decode")
+
+
+def test_workload_prefill_causal():
+    inp = W.prefill_causal()
+    rows = np.array([0, 1, 7, 8, 100, 2046, 2047, 2048, 4095, 5000, 8190, 8191])
+    g = _sampled_check(inp, rows, "prefill_causal")
+    # causal: row t has exactly t+1 finite entries
+    finite = np.isfinite(g).sum(axis=1)
+    assert np.array_equal(finite, np.arange(1, 8193))
+
+
+def test_workload_long_chunk():
+    inp = W.long_chunk()
+    rows = np.array([0, 1, 511, 1022, 1023])
+    _sampled_check(inp, rows, "long_chunk")

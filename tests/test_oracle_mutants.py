@@ -30,8 +30,9 @@ MUTANTS = [
     ("no_relu", "double rect = dot > 0.0 ? dot : 0.0;", "double rect = dot;"),
     ("sum_then_relu", "total += (double)w[h] * rect;", "total += (double)w[h] * dot;"),
     ("wrong_weight_index", "total += (double)w[h] * rect;", "total += (double)w[0] * rect;"),
-    ("key_index_shift", "half_to_double(k_s[i])", "half_to_double(k_s[(i + 1) % d])"),
-    ("key_dot_reversed", "half_to_double(k_s[i])", "half_to_double(k_s[d - 1 - i])"),
+    ("key_index_shift", "dot += q_th[i] * k_s[i];", "dot += q_th[i] * k_s[(i + 1) % d];"),
+    ("key_dot_reversed", "dot += q_th[i] * k_s[i];", "dot += q_th[i] * k_s[d - 1 - i];"),
+    ("query_head_stride_wrong", "const double *q_th = q_t + (int64_t)h * d;", "const double *q_th = q_t + (int64_t)(h % 2) * d;"),
     ("mask_inside_relu", "            if (mask)\n                v += half_to_double(mask[(int64_t)t * mask_stride_t + s]);",
      "            if (mask)\n                v = fmax(v + half_to_double(mask[(int64_t)t * mask_stride_t + s]), 0.0);"),
     ("mask_dropped", "            if (mask)\n                v += half_to_double(mask[(int64_t)t * mask_stride_t + s]);", ""),
@@ -44,6 +45,7 @@ MUTANTS = [
      "if (x->score < y->score) return -1;\n    if (x->score > y->score) return 1;"),
     ("no_padding", "idx_out[i] = -1;", "idx_out[i] = 0;"),
     ("decode_visibility_off_by_one", "(int64_t)seq_lens[r] - Q + 1 + j", "(int64_t)seq_lens[r] - Q + j"),
+    ("decode_row_order_swapped", "int64_t t = (int64_t)r * Q + j;", "int64_t t = (int64_t)j * R + r;"),
     ("decode_ignores_block_table", "(phys * block_size + s % block_size)", "((int64_t)s)"),
     ("decode_first_block_only", "s / block_size];", "0];"),
 ]
