@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark: lightning-indexer score + top-k on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
+
+One step is the whole hot path over one batch of synthetic input: the
+indexer score into a [rows, keys] f32 buffer, then the per-row top-k.  The
+timed region is exactly K steps between two synchronisations; inputs are
+resident in HBM before it starts, and several copies of them are rotated so
+that consecutive steps do not hit the 256 MB Infinity Cache.
+
+Prints ONE JSON line: throughput in visible (token, key) pairs per second,
+the roofline of the dominant kernel (its average duration measured with HIP
+events on the launch stream over its own timed loop), and the CPU oracle
+timed on a bounded sample of the same workload as a baseline.
+
+Workloads (``--config``):
+  tiny            16 tokens x 256 keys, 4 heads of 64, top-32
+  decode          32 requests x 1 query, 1024..8192 paged keys, 64 heads of 128, top-512 (default)
+  spec_decode     32 requests x 4 queries, 16384 paged keys, top-2048
+  prefill_causal  8192 tokens x 8192 keys, causal f16 mask, top-2048
+  long_chunk      1024-token chunk x 131072 keys, causal, top-2048
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+MALL_BYTES = 256 << 20
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=None)
+    ap.add_argument("--warmup", type=int, default=None)
+    ap.add_argument("--config", default="decode",
+                    choices=["tiny", "decode", "spec_decode", "prefill_causal", "long_chunk"])
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    return ap.parse_args()
+
+
+DEFAULT_STEPS = {"tiny": (2000, 200), "decode": (1000, 100), "spec_decode": (300, 30),
+                 "prefill_causal": (20, 3), "long_chunk": (10, 2)}
+
+
+def visible_pairs_rows(inp) -> np.ndarray:
+    """Visible keys per score row (entries the score defines as finite)."""
+    if hasattr(inp, "k_cache"):
+        R, Q = inp.R, inp.Q
+        sl = inp.seq_lens.astype(np.int64)
+        vis = np.empty(R * Q, dtype=np.int64)
+        for r in range(R):
+            for j in range(Q):
+                vis[r * Q + j] = min(max(sl[r] - Q + 1 + j, 0), inp.max_seq_len)
+        return vis
+    T, P = inp.T, inp.P
+    if inp.mask is not None:
+        return (~np.isneginf(inp.mask.astype(np.float32))).sum(axis=1).astype(np.int64)
+    return np.full(T, P, dtype=np.int64)
+
+
+def score_bytes_decode(inp) -> int:
+    """Algorithmic HBM bytes of one paged score launch: every key of every
+    request read once (for all heads and all query tokens), q once, the
+    weights, the block-table entries used, seq_lens, and the f32 score rows
+    written once."""
+    H, d, R, Q, bs = inp.H, inp.d, inp.R, inp.Q, inp.block_size
+    L = np.minimum(inp.seq_lens.astype(np.int64), inp.max_seq_len)
+    keys = int(L.sum()) * d * 2
+    qb = R * Q * H * d * 2
+    bt = int(np.ceil(L / bs).sum()) * 4
+    out = R * Q * inp.max_seq_len * 4
+    return keys + qb + H * 4 + bt + R * 4 + out
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}); see DESIGN.md for how the work would shard.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_attention_lightning_indexer_amd as li
+    import workloads as W
+
+    steps, warmup = DEFAULT_STEPS[args.config]
+    steps = args.steps if args.steps is not None else steps
+    warmup = args.warmup if args.warmup is not None else warmup
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    lib = li.load_library()  # raises if the HIP library is missing
+
+    gen = getattr(W, args.config)
+    inp = gen(0, poison=False) if args.config in ("decode", "spec_decode") else gen(0)
+    paged = hasattr(inp, "k_cache")
+    vis_rows = visible_pairs_rows(inp)
+    pairs = int(vis_rows.sum())
+
+    # ---- device-resident inputs, rotated copies -----------------------
+    def t(a):
+        return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    if paged:
+        base = dict(q=t(inp.q), k=t(inp.k_cache), mask=t(inp.mask))
+        shared = dict(bt=t(inp.block_table), sl=t(inp.seq_lens), w=t(inp.w))
+        n_rows, n_cols = inp.R * inp.Q, inp.max_seq_len
+    else:
+        base = dict(q=t(inp.q), k=t(inp.k), mask=t(inp.mask))
+        shared = dict(w=t(inp.w), vis=t(inp.vis_len))
+        n_rows, n_cols = inp.T, inp.P
+    copy_bytes = sum(v.numel() * v.element_size() for v in base.values() if v is not None)
+    n_copies = max(1, min(16, math.ceil(2 * MALL_BYTES / max(copy_bytes, 1))))
+    copies = [base] + [{k2: (v.clone() if v is not None else None) for k2, v in base.items()}
+                       for _ in range(n_copies - 1)]
+    k_top = inp.k_top
+    score = torch.empty((n_rows, n_cols), dtype=torch.float32, device=dev)
+    idx = torch.empty((n_rows, k_top), dtype=torch.int32, device=dev)
+    val = torch.empty((n_rows, k_top), dtype=torch.float32, device=dev)
+
+    def run_score(c):
+        if paged:
+            li.score_decode(c["q"], c["k"], shared["bt"], shared["sl"], inp.Q, inp.max_seq_len,
+                            shared["w"], c["mask"], out=score)
+        else:
+            li.score_prefill(c["q"], c["k"], shared["w"], c["mask"], shared["vis"], out=score)
+
+    def run_topk():
+        li.topk(score, k_top, idx=idx, val=val)
+
+    def step(i):
+        run_score(copies[i % n_copies])
+        run_topk()
+
+    # ---- warmup, then the timed region: exactly `steps` steps --------
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(steps):
+        step(i)
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = ev0.elapsed_time(ev1) / steps
+
+    # ---- per-kernel average durations (HIP events, same stream) -------
+    def avg_ms(fn):
+        for i in range(3):
+            fn(i)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(steps):
+            fn(i)
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    score_ms = avg_ms(lambda i: run_score(copies[i % n_copies]))
+    topk_ms = avg_ms(lambda i: run_topk())
+
+    # check the timed outputs once (cheap sanity: every row's first index is a
+    # visible key or -1)
+    first = idx[:, 0].cpu().numpy()
+    assert np.all((first >= -1) & (first < n_cols))
+
+    # ---- roofline of the dominant kernel --------------------------------
+    if score_ms >= topk_ms:
+        kern, kms = "score", score_ms
+        if paged:
+            work = score_bytes_decode(inp)
+            roof = dict(bound="hbm", achieved=work / (kms * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
+        else:
+            work = 2 * inp.H * inp.d * pairs
+            roof = dict(bound="mfma", achieved=work / (kms * 1e-3) / 1e12, peak=MFMA_F16_PEAK_TFLOPS,
+                        unit="TFLOP/s")
+    else:
+        kern, kms = "topk", topk_ms
+        work = n_rows * n_cols * 4 + n_rows * k_top * 8
+        roof = dict(bound="hbm", achieved=work / (kms * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = kern
+    roof["kernel_ms"] = kms
+
+    line = {
+        "metric": "indexer score+top-k: (token,key) pairs/s; % of MFMA or HBM roofline",
+        "value": pairs / (ms_per_step * 1e-3),
+        "unit": "pairs/s",
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": args.config, "rows": n_rows, "keys": n_cols, "heads": inp.H,
+                   "head_dim": inp.d, "k_top": k_top, "visible_pairs": pairs,
+                   "input_copies": n_copies},
+        "roofline": roof,
+        "kernels_ms": {"score": score_ms, "topk": topk_ms},
+        "wall_s": wall,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(inp, vis_rows, args.cpu_seconds)
+    text = json.dumps(line)
+    print(text, flush=True)
+    if args.out:
+        with open(args.out, "a") as f:
+            f.write(text + "\n")
+
+
+def cpu_baseline(inp, vis_rows, seconds):
+    """The CPU oracle (fp64, OpenMP over the host cores) on a bounded sample
+    of the same workload: score + top-k for a subset of rows, repeated until
+    about `seconds` of wall time; reported as visible pairs per second."""
+    import oracle
+    n_rows = len(vis_rows)
+    # rows per repetition: keep one repetition around a second on a few cores
+    budget_pairs = 400_000
+    order = np.linspace(0, n_rows - 1, num=min(n_rows, 64)).astype(np.int64)
+    rows, acc = [], 0
+    for r in order:
+        rows.append(int(r))
+        acc += int(vis_rows[r])
+        if acc >= budget_pairs:
+            break
+    if hasattr(inp, "k_cache"):
+        # whole requests: the oracle scores a request's rows together
+        reqs = sorted(set(r // inp.Q for r in rows))
+        rows = [r * inp.Q + j for r in reqs for j in range(inp.Q)]
+    rows = np.array(sorted(set(rows)))
+    sample_pairs = int(vis_rows[rows].sum())
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        s = oracle.score_rows(inp, rows)
+        oracle.topk(s, inp.k_top)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 1000:
+            break
+    return {"value": sample_pairs * reps / el, "unit": "pairs/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": f"{len(rows)} of {n_rows} score rows ({sample_pairs} visible pairs), "
+                      f"score + top-{inp.k_top}, repeated {reps}x in {el:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

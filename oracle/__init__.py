@@ -144,17 +144,18 @@ def score_rows(inp, rows, lib=None) -> np.ndarray:
     """Oracle scores for a subset of query rows only (whole key range)."""
     rows = np.asarray(rows, dtype=np.int64)
     if hasattr(inp, "k_cache"):
-        out = []
-        for t in rows:
-            r, j = divmod(int(t), inp.Q)
-            # one request, keep its own query row j by slicing q and the mask
+        # score each request touched once, then pick its rows
+        out = np.empty((len(rows), inp.max_seq_len))
+        for r in sorted(set(int(t) // inp.Q for t in rows)):
             q = inp.q[r * inp.Q:(r + 1) * inp.Q]
             m = None if inp.mask is None else inp.mask[r * inp.Q:(r + 1) * inp.Q]
             full = score_decode(q, inp.k_cache, inp.block_table[r:r + 1],
                                 inp.seq_lens[r:r + 1], inp.Q, inp.max_seq_len,
                                 inp.w, m, lib=lib)
-            out.append(full[j])
-        return np.stack(out) if out else np.empty((0, inp.max_seq_len))
+            for i, t in enumerate(rows):
+                if int(t) // inp.Q == r:
+                    out[i] = full[int(t) % inp.Q]
+        return out
     mask = None if inp.mask is None else inp.mask[rows]
     vis = None if inp.vis_len is None else inp.vis_len[rows]
     return score_prefill(inp.q[rows], inp.k, inp.w, mask, vis, lib=lib)
