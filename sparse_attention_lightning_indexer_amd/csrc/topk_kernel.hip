@@ -218,22 +218,25 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, int k_pad) {
     }
 }
 
-size_t lds_bytes(int n_cols, int k_pad, bool row_in_lds) {
-    return (size_t)kBins * 4 + (size_t)k_pad * 8 + 256 + (row_in_lds ? (size_t)n_cols * 4 : 0);
-}
-
-int max_lds_per_block() {
-    static int cached[64];
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 65536;
-    if (cached[dev] == 0) {
-        int v = 0;
-        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess || v <= 0)
-            v = 65536;
-        cached[dev] = v;
-    }
-    return cached[dev];
-}
+// ---------------------------------------------------------------------------
+// Register-resident variant for rows of up to THREADS*E keys.
+//
+//  * Each thread holds E keys, striped (key t + THREADS*j): coalesced loads,
+//    index order (j, thread).
+//  * Radix select with adaptive 12-bit digits: the bits shared by the row's
+//    largest and smallest selectable keys are skipped; each pass resolves the
+//    12 bits just below the prefix found so far and stops as soon as the bin
+//    holding the k-th key is taken whole.  Histograms are double buffered and
+//    the threshold bin is found by a two-level (wave, lane) search, so a pass
+//    costs three barriers.
+//  * Compaction keeps index order with one scan over a (j, wave) table.
+//  * Ordering: every selected key lies in [threshold prefix, row max], so a
+//    12-bit bucket just below their common prefix spreads them out.  After a
+//    counting-sort scatter into buckets, each element's final position is
+//    its bucket's start plus the number of bucket members that precede it in
+//    (key descending, index ascending) order.  Rows whose largest bucket is
+//    bigger than kMaxBucket (heavy ties) use a plain bitonic sort instead.
+// ---------------------------------------------------------------------------
 
 template <typename K>
 hipError_t allow_lds(K kern, size_t bytes) {
@@ -244,6 +247,364 @@ hipError_t allow_lds(K kern, size_t bytes) {
     return e;
 }
 
+constexpr int kMaxBucket = 64;
+
+template <int THREADS>
+__device__ __forceinline__ int scan_excl(int v, int *tmp, int &total) {
+    constexpr int NW = THREADS / 64;
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int y = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += y;
+    }
+    if (lane == 63) tmp[wid] = incl;
+    __syncthreads();
+    int off = 0, tot = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int x = tmp[w];
+        off += w < wid ? x : 0;
+        tot += x;
+    }
+    __syncthreads();
+    total = tot;
+    return off + incl - v;
+}
+
+// Finds, over nb bins read in descending order, the bin where the running
+// count first reaches `need`.  Returns (bin, need within the bin, bin count)
+// through sc[0..2]; ends with a barrier.  Uses sc[4..4+NW).
+template <int THREADS>
+__device__ void threshold_bin(const uint32_t *h, int nb, int need, int *sc) {
+    constexpr int NW = THREADS / 64;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    constexpr int MAXPER = 4096 / THREADS;
+    const int per = nb > THREADS ? nb / THREADS : 1;  // bins per thread
+    int c[MAXPER];
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < MAXPER; ++q) {
+        c[q] = 0;
+        const int r = tid * per + q;
+        if (q < per && r < nb) {
+            c[q] = (int)h[nb - 1 - r];
+            local += c[q];
+        }
+    }
+    int wsum = local;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o, 64);
+    if (lane == 0) sc[4 + wid] = wsum;
+    __syncthreads();
+    // the wave whose bins contain the crossing, and the count before it
+    int before = 0, wstar = NW;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        const int x = sc[4 + w];
+        if (wstar == NW) {
+            if (before + x >= need) wstar = w;
+            else before += x;
+        }
+    }
+    if (wid == wstar) {
+        int incl = local;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int y = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        int acc = before + incl - local;
+#pragma unroll
+        for (int q = 0; q < MAXPER; ++q) {
+            if (q < per && acc < need && acc + c[q] >= need) {
+                sc[0] = nb - 1 - (tid * per + q);
+                sc[1] = need - acc;
+                sc[2] = c[q];
+            }
+            acc += c[q];
+        }
+    }
+    __syncthreads();
+}
+
+template <int THREADS, int E>
+__global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) {
+    constexpr int NW = THREADS / 64;
+    // LDS: hist0 | hist1 (16 KB each) | sel | tmp (p2*8 each) | table | scalars
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint32_t *hist0 = reinterpret_cast<uint32_t *>(smem);
+    uint32_t *hist1 = reinterpret_cast<uint32_t *>(smem + 16384);
+    unsigned long long *sel = reinterpret_cast<unsigned long long *>(smem + 32768);
+    unsigned long long *tmp = reinterpret_cast<unsigned long long *>(smem + 32768 + 8 * (size_t)p2);
+    uint32_t *table = reinterpret_cast<uint32_t *>(smem + 32768 + 16 * (size_t)p2);
+    int *sc = reinterpret_cast<int *>(smem + 32768 + 16 * (size_t)p2 + 4 * E * NW);
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int t = blockIdx.x;
+    const float *row = a.score + (int64_t)t * a.score_st;
+    int n = a.n_cols;
+    if (a.row_len) n = min(max(a.row_len[t], 0), n);
+    const int k = a.k_top;
+
+    uint32_t key[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        const int i = tid + THREADS * j;
+        key[j] = i < n ? order_key(row[i]) : 0u;
+    }
+    for (int i = tid; i < 4096; i += THREADS) hist0[i] = 0u;
+
+    // ---- count, min and max of the selectable keys ---------------------
+    int cnt = 0;
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        if (key[j]) {
+            ++cnt;
+            mn = min(mn, key[j]);
+            mx = max(mx, key[j]);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        cnt += __shfl_xor(cnt, o, 64);
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+    }
+    if (lane == 0) {
+        sc[8 + wid] = cnt;
+        sc[8 + NW + wid] = (int)mn;
+        sc[8 + 2 * NW + wid] = (int)mx;
+    }
+    __syncthreads();
+    int nsel = 0;
+    mn = 0xffffffffu;
+    mx = 0u;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+        nsel += sc[8 + w];
+        mn = min(mn, (uint32_t)sc[8 + NW + w]);
+        mx = max(mx, (uint32_t)sc[8 + 2 * NW + w]);
+    }
+
+    // ---- adaptive radix select -----------------------------------------
+    const bool all = nsel <= k;
+    uint32_t prefix = 0u, pmask = 0u;
+    int need = k;
+    if (!all) {
+        const uint32_t diff = mn ^ mx;
+        int pos = diff ? 32 - __clz(diff) : 0;  // bits below the common prefix
+        pmask = pos >= 32 ? 0u : ~((1u << pos) - 1u);
+        prefix = mx & pmask;
+        int pass = 0;
+        while (pos > 0) {
+            const int width = pos < 12 ? pos : 12;
+            const int shift = pos - width;
+            const int nb = 1 << width;
+            uint32_t *h = (pass & 1) ? hist1 : hist0;
+            uint32_t *hn = (pass & 1) ? hist0 : hist1;
+#pragma unroll
+            for (int j = 0; j < E; ++j) {
+                const uint32_t u = key[j];
+                if (u && (u & pmask) == prefix) atomicAdd(&h[(u >> shift) & (nb - 1)], 1u);
+            }
+            for (int i = tid; i < 4096; i += THREADS) hn[i] = 0u;  // next pass
+            __syncthreads();
+            threshold_bin<THREADS>(h, nb, need, sc);
+            const uint32_t digit = (uint32_t)sc[0];
+            need = sc[1];
+            const int cbin = sc[2];
+            prefix |= digit << shift;
+            pmask |= (uint32_t)(nb - 1) << shift;
+            pos = shift;
+            ++pass;
+            if (cbin == need) break;  // the whole bin is taken
+        }
+    }
+    const int count_gt = all ? nsel : k - need;
+    const int take_eq = all ? 0 : need;
+    const int total_sel = all ? nsel : k;
+
+    // ---- index-ordered compaction into sel[] ---------------------------
+    const unsigned long long below = lanes_below(lane);
+    auto is_gt = [&](uint32_t u) { return all ? u != 0u : (u & pmask) > prefix; };
+    auto is_eq = [&](uint32_t u) { return !all && u != 0u && (u & pmask) == prefix; };
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        const unsigned long long mg = __builtin_amdgcn_ballot_w64(is_gt(key[j]));
+        const unsigned long long me = __builtin_amdgcn_ballot_w64(is_eq(key[j]));
+        if (lane == 0) table[j * NW + wid] = (uint32_t)__popcll(mg) | ((uint32_t)__popcll(me) << 16);
+    }
+    __syncthreads();
+    if (wid == 0) {
+        constexpr int N = E * NW;
+        constexpr int PER = (N + 63) / 64;
+        uint32_t v[PER];
+        uint32_t s = 0;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int e = lane * PER + q;
+            v[q] = e < N ? table[e] : 0u;
+            s += v[q];
+        }
+        uint32_t incl = s;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
+            if (lane >= o) incl += y;
+        }
+        uint32_t run = incl - s;
+#pragma unroll
+        for (int q = 0; q < PER; ++q) {
+            const int e = lane * PER + q;
+            if (e < N) table[e] = run;
+            run += v[q];
+        }
+    }
+    // bucket histogram of the next phase lives in hist0/hist1's free buffer
+    uint32_t *bh = hist0;
+    uint32_t *bstart = hist1;
+    for (int i = tid; i < 4096; i += THREADS) bh[i] = 0u;
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        const uint32_t base = table[j * NW + wid];
+        const bool gt = is_gt(key[j]), eq = is_eq(key[j]);
+        const unsigned long long mg = __builtin_amdgcn_ballot_w64(gt);
+        const unsigned long long me = __builtin_amdgcn_ballot_w64(eq);
+        const unsigned long long packed =
+            ((unsigned long long)key[j] << 32) | (uint32_t)(~(uint32_t)(tid + THREADS * j));
+        if (gt) sel[(base & 0xffffu) + __popcll(mg & below)] = packed;
+        if (eq) {
+            const int r = (int)(base >> 16) + __popcll(me & below);
+            if (r < take_eq) sel[count_gt + r] = packed;
+        }
+    }
+    __syncthreads();
+
+    int32_t *idx_out = a.idx + (int64_t)t * a.out_st;
+    float *val_out = a.val ? a.val + (int64_t)t * a.out_st : nullptr;
+    auto emit = [&](int pos, unsigned long long e) {
+        const int s = (int)(~(uint32_t)(e & 0xffffffffull));
+        idx_out[pos] = s;
+        if (val_out) val_out[pos] = row[s];
+    };
+    for (int j = total_sel + tid; j < k; j += THREADS) {
+        idx_out[j] = -1;
+        if (val_out) val_out[j] = -INFINITY;
+    }
+
+    // ---- ordering: bucket by the 12 bits below the selection's prefix ---
+    const uint32_t lo_key = all ? mn : prefix;  // every selected key is in [lo_key, mx]
+    const uint32_t d2 = lo_key ^ mx;
+    if (d2 == 0u) {
+        // all selected keys equal: index order is the answer
+        for (int j = tid; j < total_sel; j += THREADS) emit(j, sel[j]);
+        return;
+    }
+    const int pos2 = 32 - __clz(d2);
+    const int bshift = pos2 > 12 ? pos2 - 12 : 0;
+    const int bnb = 1 << (pos2 - bshift);
+    for (int j = tid; j < total_sel; j += THREADS)
+        atomicAdd(&bh[(uint32_t)(sel[j] >> (32 + bshift)) & (bnb - 1)], 1u);
+    __syncthreads();
+    // descending exclusive scan of bucket counts -> start offsets; max count
+    constexpr int MAXPER = 4096 / THREADS;
+    const int per = bnb > THREADS ? bnb / THREADS : 1;
+    int c4[MAXPER];
+    int local = 0, cmax = 0;
+#pragma unroll
+    for (int q = 0; q < MAXPER; ++q) {
+        c4[q] = 0;
+        const int r = tid * per + q;
+        if (q < per && r < bnb) {
+            c4[q] = (int)bh[bnb - 1 - r];
+            local += c4[q];
+            cmax = max(cmax, c4[q]);
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) cmax = max(cmax, __shfl_xor(cmax, o, 64));
+    if (lane == 0) sc[8 + wid] = cmax;
+    int total;
+    int run = scan_excl<THREADS>(local, sc + 64, total);  // its barriers publish sc[8..]
+#pragma unroll
+    for (int q = 0; q < MAXPER; ++q) {
+        const int r = tid * per + q;
+        if (q < per && r < bnb) bstart[bnb - 1 - r] = (uint32_t)run;
+        run += c4[q];
+    }
+    int bmax = 0;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) bmax = max(bmax, sc[8 + w]);
+
+    if (bmax <= kMaxBucket) {
+        // scatter into buckets (order inside a bucket arbitrary), then rank
+        for (int i = tid; i < bnb; i += THREADS) bh[i] = 0u;  // reuse as cursors
+        __syncthreads();
+        for (int j = tid; j < total_sel; j += THREADS) {
+            const unsigned long long e = sel[j];
+            const uint32_t b = (uint32_t)(e >> (32 + bshift)) & (bnb - 1);
+            tmp[bstart[b] + atomicAdd(&bh[b], 1u)] = e;
+        }
+        __syncthreads();
+        for (int j = tid; j < total_sel; j += THREADS) {
+            const unsigned long long e = tmp[j];
+            const uint32_t b = (uint32_t)(e >> (32 + bshift)) & (bnb - 1);
+            const int s0 = (int)bstart[b];
+            const int c = (int)bh[b];
+            int rank = 0;
+            for (int q = 0; q < c; ++q) rank += tmp[s0 + q] > e;
+            emit(s0 + rank, e);
+        }
+        return;
+    }
+
+    // ---- heavy ties: bitonic sort of sel[] in LDS, descending ----------
+    int P2 = 1;
+    while (P2 < total_sel) P2 <<= 1;
+    for (int i = total_sel + tid; i < P2; i += THREADS) sel[i] = 0ull;
+    __syncthreads();
+    for (int size = 2; size <= P2; size <<= 1) {
+        for (int stride = size >> 1; stride > 0; stride >>= 1) {
+            for (int q = tid; q < (P2 >> 1); q += THREADS) {
+                const int i = 2 * q - (q & (stride - 1));
+                const int l = i + stride;
+                const unsigned long long x = sel[i], y = sel[l];
+                const bool desc = (i & size) == 0;
+                if (desc ? (x < y) : (x > y)) {
+                    sel[i] = y;
+                    sel[l] = x;
+                }
+            }
+            __syncthreads();
+        }
+    }
+    for (int j = tid; j < total_sel; j += THREADS) emit(j, sel[j]);
+}
+
+template <int THREADS, int E>
+size_t rows_lds_bytes(int p2) {
+    return 32768 + 16 * (size_t)p2 + 4 * (size_t)E * (THREADS / 64) + 4 * (64 + THREADS / 64) + 16;
+}
+
+template <int THREADS, int E>
+hipError_t launch_rows(const TopkArgs &a, int k_pad, hipStream_t stream) {
+    auto kern = topk_rows_kernel<THREADS, E>;
+    const size_t bytes = rows_lds_bytes<THREADS, E>(k_pad);
+    hipError_t e = allow_lds(kern, bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, dim3(a.n_rows), dim3(THREADS), bytes, stream, a, k_pad);
+    return hipGetLastError();
+}
+
+size_t lds_bytes(int n_cols, int k_pad, bool row_in_lds) {
+    return (size_t)kBins * 4 + (size_t)k_pad * 8 + 256 + (row_in_lds ? (size_t)n_cols * 4 : 0);
+}
+
+
 }  // namespace
 
 size_t topk_workspace_bytes(int, int, int) { return 0; }
@@ -252,15 +613,22 @@ hipError_t launch_topk(const TopkArgs &a, void *, hipStream_t stream) {
     if (a.n_rows <= 0 || a.k_top <= 0) return hipSuccess;
     int k_pad = 1;
     while (k_pad < a.k_top) k_pad <<= 1;
-    const size_t in_lds = lds_bytes(a.n_cols, k_pad, true);
-    if ((int)in_lds <= max_lds_per_block()) {
-        auto kern = topk_kernel<true>;
-        hipError_t e = allow_lds(kern, in_lds);
-        if (e == hipSuccess) {
-            hipLaunchKernelGGL(kern, dim3(a.n_rows), dim3(kThreads), in_lds, stream, a, k_pad);
-            return hipGetLastError();
-        }
-        (void)hipGetLastError();  // fall through to the streaming variant
+    const int n = a.n_cols;
+    // many rows: 512-thread workgroups so that two rows share a compute unit;
+    // few rows: 1024 threads per row for the shortest latency
+    const bool many = a.n_rows >= 2 * device_cu_count();
+    if (many && n <= 512 * 16) {
+        if (n <= 512 * 2) return launch_rows<512, 2>(a, k_pad, stream);
+        if (n <= 512 * 4) return launch_rows<512, 4>(a, k_pad, stream);
+        if (n <= 512 * 8) return launch_rows<512, 8>(a, k_pad, stream);
+        return launch_rows<512, 16>(a, k_pad, stream);
+    }
+    if (n <= 1024 * 16) {
+        if (n <= 1024) return launch_rows<1024, 1>(a, k_pad, stream);
+        if (n <= 2048) return launch_rows<1024, 2>(a, k_pad, stream);
+        if (n <= 4096) return launch_rows<1024, 4>(a, k_pad, stream);
+        if (n <= 8192) return launch_rows<1024, 8>(a, k_pad, stream);
+        return launch_rows<1024, 16>(a, k_pad, stream);
     }
     const size_t streamed = lds_bytes(a.n_cols, k_pad, false);
     auto kern = topk_kernel<false>;

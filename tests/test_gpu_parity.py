@@ -182,15 +182,22 @@ def test_topk_row_len_and_short_rows():
         check_topk_exact(gi, gv, s, k, row_len, where=f"row_len k={k}")
 
 
-@pytest.mark.parametrize("n_cols", [1, 255, 8192, 16384, 16385, 40000, 131072])
+@pytest.mark.parametrize("n_cols", [1, 255, 1024, 1025, 2048, 4096, 5000, 8192, 12000, 16384, 16385,
+                                    40000, 131072])
 def test_topk_row_lengths(n_cols):
     rng = np.random.default_rng(n_cols)
-    rows = 6
+    rows = 8
     s = (rng.standard_normal((rows, n_cols)) * 10).astype(np.float32)
-    s[:, ::7] = np.round(s[:, ::7])          # exact ties
-    s[0, :] = 1.0                             # a row of equal scores
+    s[:, ::7] = np.round(s[:, ::7])           # exact ties
+    s[0, :] = 1.0                              # a row of equal scores
     s[1, rng.random(n_cols) < 0.5] = -np.inf
-    for k in (1, 64, 2048):
+    s[2] = 24.0 + rng.random(n_cols).astype(np.float32)   # narrow: one binade
+    s[3] = -np.abs(s[3])                       # all negative
+    s[4, rng.random(n_cols) < 0.9] = 0.0       # mostly exact zeros (and -0)
+    s[4, rng.random(n_cols) < 0.3] = -0.0
+    s[5, :] = -np.inf                          # nothing selectable
+    s[6, rng.random(n_cols) < 0.05] = np.nan
+    for k in (1, 31, 64, 512, 2048):
         gi, gv = gpu_topk(dev(s), k)
         check_topk_exact(gi, gv, s, k, where=f"n_cols={n_cols} k={k}")
 
