@@ -198,10 +198,13 @@ lidx::ScoreArgs decode_args(const void *q, int64_t q_stride_t, int64_t q_stride_
 
 indexer_status run_score(lidx::ScoreArgs &a, int n_heads, int head_dim, bool paged, int n_requests,
                          hipStream_t stream) {
-    lidx::ScorePlan p = lidx::plan_score(a, n_heads, head_dim, paged, n_requests);
+    lidx::ScorePlan p = paged ? lidx::plan_decode(a, n_heads, head_dim, n_requests)
+                              : lidx::plan_score(a, n_heads, head_dim);
     if ((int64_t)a.n_row_groups * a.n_chunks > INT32_MAX)
         return fail(INDEXER_EINVAL, "problem too large for one launch");
-    return hip_status(lidx::launch_score(a, p, n_heads, head_dim, paged, stream), "score kernel launch");
+    hipError_t e = paged ? lidx::launch_decode(a, p, n_heads, head_dim, stream)
+                         : lidx::launch_score(a, p, n_heads, head_dim, stream);
+    return hip_status(e, "score kernel launch");
 }
 
 indexer_status run_topk(const float *score, int64_t score_stride_t, int32_t n_rows, int32_t n_cols,

@@ -44,15 +44,21 @@ struct ScorePlan {
     int rows_per_group;
     int nc, nbw;
     int tile_keys;
+    bool split;  // paged decode: one query row, heads split over the row slots
     size_t lds_bytes;
     dim3 grid;
 };
 
 bool score_shape_supported(int n_heads, int head_dim);
-// Fills the launch-geometry fields of `a` and returns the plan.
-ScorePlan plan_score(ScoreArgs &a, int n_heads, int head_dim, bool paged, int n_requests);
+// Contiguous keys (score_kernel.hip).  Fills the launch-geometry fields of
+// `a` and returns the plan.
+ScorePlan plan_score(ScoreArgs &a, int n_heads, int head_dim);
 hipError_t launch_score(const ScoreArgs &a, const ScorePlan &p, int n_heads,
-                        int head_dim, bool paged, hipStream_t stream);
+                        int head_dim, hipStream_t stream);
+// Paged keys (decode_kernel.hip).
+ScorePlan plan_decode(ScoreArgs &a, int n_heads, int head_dim, int n_requests);
+hipError_t launch_decode(const ScoreArgs &a, const ScorePlan &p, int n_heads,
+                         int head_dim, hipStream_t stream);
 
 struct TopkArgs {
     const float *score;

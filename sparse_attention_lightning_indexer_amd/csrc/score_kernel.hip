@@ -27,70 +27,25 @@
 //    (scalar) operand, and the sum over heads stays inside each lane: no
 //    cross-lane reduction and no per-head [rows, heads, keys] tensor.
 //  * Visibility: the workgroup first bounds its key range by the rows'
-//    visible prefixes (vis_len, or seq_len - Q + 1 + j for paged decode) and,
+//    visible prefixes (vis_len) and,
 //    when a mask is given, by its last non -inf entry; key tiles past that
 //    bound are filled with -inf without being loaded.  A wave whose entries
 //    in a 32-key block are all invisible skips the MFMAs for that block.
-//  * Paged keys: the workgroup's block-table entries are staged in LDS once;
-//    slots past a request's length are never addressed.
-#include "internal.h"
-
+//
+// This kernel serves contiguous keys (prefill, chunked prefill); paged decode
+// has its own latency-oriented kernel (decode_kernel.hip).
 #include <math.h>
+
+#include "device_common.h"
+#include "internal.h"
 
 namespace lidx {
 namespace {
 
-typedef _Float16 half8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 
-template <int H, int D>
-struct Geo {
-    static_assert(H == 4 || H == 8 || (H % 16 == 0 && H <= 64), "head count");
-    static_assert(D == 64 || D == 128, "head dim");
-    static constexpr int HPB = H < 16 ? H : 16;   // heads per M-block
-    static constexpr int TPB = 32 / HPB;          // query rows per M-block (= per wave)
-    static constexpr int MBLK = H / HPB;          // M-blocks per wave
-    static constexpr int G = HPB / 4;             // 4-register groups per row slot
-    static constexpr int SLOTS = 4 / G;           // query rows held by one lane
-    static constexpr int KSTEPS = D / 16;         // MFMA K steps
-    static constexpr int CPR = D / 8;             // 16-byte chunks per key row
-    static constexpr int ROWB = 2 * D;            // bytes per key row in LDS
-    static constexpr int ROWS_PER_256B = 256 / ROWB;
-};
-
-// Swizzled position of a key row's 16-byte chunk: the chunk index is XORed
-// with a function of the row so that the rows read by one 16-lane phase land
-// in distinct 16-byte bank groups.
-template <int D>
-__device__ __forceinline__ int swz(int n) {
-    return (n / Geo<4, D>::ROWS_PER_256B) & (Geo<4, D>::CPR - 1);
-}
-
-__device__ __forceinline__ bool half_is_neg_inf(_Float16 h) {
-    return __builtin_bit_cast(unsigned short, h) == 0xfc00u;
-}
-
-__device__ __forceinline__ void wait_vmem_all() {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-}
-
-// max(x, 0) as one integer max on the bit pattern: a negative float (or -0)
-// is a negative int32 and becomes +0; a non-negative float is unchanged.  One
-// v_max_i32 per accumulator (fmaxf would add a NaN-quieting v_max first).
-// Inline asm is avoided here on purpose: the hazard checks between MFMA
-// results and their VALU readers only see compiler-visible instructions.
-__device__ __forceinline__ float relu(float x) {
-    return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
-}
-
-// Per-head weights are read through the constant address space so that they
-// load with scalar instructions and feed the epilogue FMAs as SGPR operands.
-typedef const __attribute__((address_space(4))) float const_f32;
-
-template <int H, int D, bool PAGED, int NBW>
+template <int H, int D, int NBW>
 __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
     using G = Geo<H, D>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -118,23 +73,11 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
     const int key_lo = chunk_id * a.chunk;
     const int key_hi = min(a.n_cols, key_lo + a.chunk);
 
-    int seq_len = 0;
-    int key_exist = a.n_cols;  // keys that may be addressed
-    if constexpr (PAGED) {
-        seq_len = max(0, a.seq_lens[req]);
-        key_exist = min(seq_len, a.n_cols);
-    }
     auto row_vis = [&](int t) -> int {
-        if constexpr (PAGED) {
-            const int j = t - req_row0;
-            return min(max(seq_len - a.q_per_req + 1 + j, 0), a.n_cols);
-        } else {
-            return a.vis_len ? min(max(a.vis_len[t], 0), a.n_cols) : a.n_cols;
-        }
+        return a.vis_len ? min(max(a.vis_len[t], 0), a.n_cols) : a.n_cols;
     };
 
     int *misc = reinterpret_cast<int *>(smem + 2 * tile_bytes);
-    int *bt_lds = misc + 4;
 
     // ---- bound the key range: prefix lengths, then the mask ------------
     if (tid == 0) {
@@ -183,18 +126,7 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
         bound = misc[1];
     }
 
-    const int load_limit = min(bound, key_exist);
-    int b_lo = 0;
-    if constexpr (PAGED) {
-        // stage the block ids of the keys this workgroup will load
-        const int bs = a.block_size;
-        b_lo = key_lo / bs;
-        const int b_hi = load_limit > key_lo ? (load_limit + bs - 1) / bs : b_lo;
-        for (int i = tid; i < b_hi - b_lo; i += kThreads)
-            bt_lds[i] = a.block_table[(int64_t)req * a.bt_stride + b_lo + i];
-        __syncthreads();
-    }
-
+    const int load_limit = bound;  // keys past it are visible to no row
     const int n_tiles = bound > key_lo ? (bound - key_lo + NK - 1) / NK : 0;
 
     // ---- q fragments (A operand) for this wave's rows -------------------
@@ -233,22 +165,7 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
         out_vis[j] = out_t[j] < row_hi ? row_vis(out_t[j]) : 0;
     }
 
-    auto key_src = [&](int s) -> const _Float16 * {
-        if constexpr (PAGED) {
-            int blk, slot;
-            if (a.bs_shift >= 0) {
-                blk = s >> a.bs_shift;
-                slot = s - (blk << a.bs_shift);
-            } else {
-                blk = s / a.block_size;
-                slot = s - blk * a.block_size;
-            }
-            const int64_t phys = bt_lds[blk - b_lo];
-            return a.k + (phys * a.block_size + slot) * a.k_ss;
-        } else {
-            return a.k + (int64_t)s * a.k_ss;
-        }
-    };
+    auto key_src = [&](int s) -> const _Float16 * { return a.k + (int64_t)s * a.k_ss; };
 
     auto issue_tile = [&](int tile, int buf) {
         const int s0 = key_lo + tile * NK;
@@ -412,15 +329,15 @@ hipError_t allow_lds(K kern, size_t bytes) {
     return e;
 }
 
-template <int H, int D, bool PAGED>
+template <int H, int D>
 hipError_t launch_hd(const ScoreArgs &a, const ScorePlan &p, hipStream_t stream) {
     if (p.nbw == 2) {
-        auto kern = score_kernel<H, D, PAGED, 2>;
+        auto kern = score_kernel<H, D, 2>;
         hipError_t e = allow_lds(kern, p.lds_bytes);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, p.grid, dim3(kThreads), p.lds_bytes, stream, a);
     } else {
-        auto kern = score_kernel<H, D, PAGED, 1>;
+        auto kern = score_kernel<H, D, 1>;
         hipError_t e = allow_lds(kern, p.lds_bytes);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, p.grid, dim3(kThreads), p.lds_bytes, stream, a);
@@ -428,20 +345,9 @@ hipError_t launch_hd(const ScoreArgs &a, const ScorePlan &p, hipStream_t stream)
     return hipGetLastError();
 }
 
-template <int H, bool PAGED>
+template <int H>
 hipError_t launch_h(const ScoreArgs &a, const ScorePlan &p, int D, hipStream_t stream) {
-    return D == 64 ? launch_hd<H, 64, PAGED>(a, p, stream) : launch_hd<H, 128, PAGED>(a, p, stream);
-}
-
-template <bool PAGED>
-hipError_t launch_paged(const ScoreArgs &a, const ScorePlan &p, int H, int D, hipStream_t stream) {
-    switch (H) {
-        case 4: return launch_h<4, PAGED>(a, p, D, stream);
-        case 8: return launch_h<8, PAGED>(a, p, D, stream);
-        case 16: return launch_h<16, PAGED>(a, p, D, stream);
-        case 32: return launch_h<32, PAGED>(a, p, D, stream);
-        default: return launch_h<64, PAGED>(a, p, D, stream);
-    }
+    return D == 64 ? launch_hd<H, 64>(a, p, stream) : launch_hd<H, 128>(a, p, stream);
 }
 
 }  // namespace
@@ -452,7 +358,7 @@ bool score_shape_supported(int n_heads, int head_dim) {
     return h_ok && d_ok;
 }
 
-ScorePlan plan_score(ScoreArgs &a, int n_heads, int head_dim, bool paged, int n_requests) {
+ScorePlan plan_score(ScoreArgs &a, int n_heads, int head_dim) {
     ScorePlan p{};
     const int hpb = n_heads < 16 ? n_heads : 16;
     const int tpb = 32 / hpb;
@@ -466,7 +372,7 @@ ScorePlan plan_score(ScoreArgs &a, int n_heads, int head_dim, bool paged, int n_
     p.rows_per_group = ng * tpb;
     a.nc = p.nc;
     a.groups_per_req = rows > 0 ? (rows + p.rows_per_group - 1) / p.rows_per_group : 0;
-    a.n_row_groups = a.groups_per_req * (paged ? n_requests : 1);
+    a.n_row_groups = a.groups_per_req;
 
     // keys per workgroup: aim for a few workgroups per compute unit
     const int cus = device_cu_count();
@@ -481,17 +387,19 @@ ScorePlan plan_score(ScoreArgs &a, int n_heads, int head_dim, bool paged, int n_
     if (a.n_chunks < 1) a.n_chunks = 1;
 
     const size_t tile_bytes = (size_t)p.tile_keys * 2 * head_dim;
-    size_t bt_entries = 0;
-    if (paged) bt_entries = (size_t)(a.chunk + a.block_size - 1) / a.block_size + 2;
-    p.lds_bytes = 2 * tile_bytes + 16 + 4 * bt_entries;
+    p.lds_bytes = 2 * tile_bytes + 16;
     p.grid = dim3((unsigned)(a.n_row_groups * a.n_chunks));
     return p;
 }
 
-hipError_t launch_score(const ScoreArgs &a, const ScorePlan &p, int n_heads, int head_dim,
-                        bool paged, hipStream_t stream) {
-    if (paged) return launch_paged<true>(a, p, n_heads, head_dim, stream);
-    return launch_paged<false>(a, p, n_heads, head_dim, stream);
+hipError_t launch_score(const ScoreArgs &a, const ScorePlan &p, int n_heads, int head_dim, hipStream_t stream) {
+    switch (n_heads) {
+        case 4: return launch_h<4>(a, p, head_dim, stream);
+        case 8: return launch_h<8>(a, p, head_dim, stream);
+        case 16: return launch_h<16>(a, p, head_dim, stream);
+        case 32: return launch_h<32>(a, p, head_dim, stream);
+        default: return launch_h<64>(a, p, head_dim, stream);
+    }
 }
 
 }  // namespace lidx
