@@ -57,29 +57,62 @@ __device__ __forceinline__ void wait_vmem_all() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }
 
+// s_waitcnt vmcnt(0) through the builtin: the compiler's own wait insertion
+// sees it and knows that every earlier load into registers has completed, so
+// it adds no waits of its own before their later uses.
+__device__ __forceinline__ void wait_vmem_all_known() {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) expcnt(7) lgkmcnt(15)
+}
+
+// Workgroup barrier ordering LDS accesses only.  __syncthreads() carries a
+// workgroup-scope release fence, and the compiler counts direct-to-LDS loads
+// as pending LDS writes under that fence: it would wait for every load in
+// flight (vmcnt(0)) at each barrier and drain the load pipelines.  Kernels
+// that use this barrier wait for their direct-to-LDS loads explicitly.
+__device__ __forceinline__ void lds_barrier() {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Wait until at most n vector-memory operations of this wave are pending.
 // Loads complete in issue order, so this waits for everything but the n most
-// recent loads.  n is rounded down to an encodable step (waiting longer is
-// always safe).
+// recent loads.  n is wave-uniform; counts up to 31 are exact (the pipelines
+// here keep fewer than that behind the oldest load they wait for), larger
+// ones are rounded down to 32 or 48 (waiting longer is always safe).
 __device__ __forceinline__ void wait_vmem_below(int n) {
-#define LIDX_WAIT(N) asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory")
-    if (n >= 48) LIDX_WAIT(48);
-    else if (n >= 32) LIDX_WAIT(32);
-    else if (n >= 24) LIDX_WAIT(24);
-    else if (n >= 16) LIDX_WAIT(16);
-    else if (n >= 12) LIDX_WAIT(12);
-    else if (n >= 8) LIDX_WAIT(8);
-    else if (n >= 6) LIDX_WAIT(6);
-    else if (n >= 4) LIDX_WAIT(4);
-    else if (n >= 3) LIDX_WAIT(3);
-    else if (n >= 2) LIDX_WAIT(2);
-    else if (n >= 1) LIDX_WAIT(1);
-    else LIDX_WAIT(0);
-#undef LIDX_WAIT
+#define LIDX_W(N) \
+    case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
+    switch (n < 0 ? 0 : n) {
+        LIDX_W(0) LIDX_W(1) LIDX_W(2) LIDX_W(3) LIDX_W(4) LIDX_W(5) LIDX_W(6) LIDX_W(7)
+        LIDX_W(8) LIDX_W(9) LIDX_W(10) LIDX_W(11) LIDX_W(12) LIDX_W(13) LIDX_W(14) LIDX_W(15)
+        LIDX_W(16) LIDX_W(17) LIDX_W(18) LIDX_W(19) LIDX_W(20) LIDX_W(21) LIDX_W(22) LIDX_W(23)
+        LIDX_W(24) LIDX_W(25) LIDX_W(26) LIDX_W(27) LIDX_W(28) LIDX_W(29) LIDX_W(30) LIDX_W(31)
+        default:
+            if (n >= 48) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
+            else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+            break;
+    }
+#undef LIDX_W
 }
+
+// LDS pointer types with the address space spelled out, so that LDS accesses
+// are never lowered to flat accesses (which would also count in vmcnt).
+typedef __attribute__((address_space(3))) unsigned char lds_u8;
+typedef __attribute__((address_space(3))) int lds_i32;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) half8 lds_half8;
 
 __device__ __forceinline__ void dma16(const void *src, void *lds) {
     __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void dma16(const void *src, lds_u8 *lds) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 16, 0, 0);
+}
+
+__device__ __forceinline__ void dma4(const void *src, lds_i32 *lds) {
+    __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds, 4, 0, 0);
 }
 
 }  // namespace lidx

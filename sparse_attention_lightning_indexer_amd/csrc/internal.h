@@ -44,7 +44,8 @@ struct ScorePlan {
     int rows_per_group;
     int nc, nbw;
     int tile_keys;
-    bool split;  // paged decode: one query row, heads split over the row slots
+    bool split;   // paged decode: one query row, heads split over the row slots
+    bool stream;  // paged decode: persistent streaming kernel
     size_t lds_bytes;
     dim3 grid;
 };

@@ -111,6 +111,31 @@ def test_random_decode(R, Q, H, d, bs, lo, hi, k_top):
     _full_check(inp, inp.name)
 
 
+# Larger cases for the persistent decode kernel: each workgroup gets many
+# key tiles spanning several row groups (and, with one query row, more tiles
+# than its score staging area holds); the last two shapes take the chunked
+# kernel instead (block size below 4, more than 2048 row groups).
+STREAM_CASES = [
+    # R, Q, H, d, block_size, len_lo, len_hi, k_top
+    (700, 1, 64, 128, 64, 1, 1500, 64),      # many short requests per workgroup
+    (48, 1, 64, 128, 64, 9000, 14000, 128),  # > 16 tiles per workgroup: staging flushes
+    (300, 4, 64, 128, 16, 4, 1200, 32),      # general mapping: q reloaded per row group
+    (200, 2, 32, 64, 37, 1, 3000, 40),       # block size not a power of two
+    (100, 3, 8, 128, 4, 1, 2000, 20),        # smallest block size of the persistent kernel
+    (40, 16, 4, 64, 16, 100, 3000, 24),      # 16 rows per group: a flush every 2 tiles
+    (60, 9, 64, 128, 64, 9, 2500, 16),       # two row groups per request
+    (50, 1, 16, 64, 2, 1, 800, 10),          # block size 2: chunked kernel
+    (2100, 1, 4, 64, 16, 1, 200, 8),         # > 2048 row groups: chunked kernel
+]
+
+
+@pytest.mark.parametrize("R,Q,H,d,bs,lo,hi,k_top", STREAM_CASES,
+                         ids=[f"R{c[0]}Q{c[1]}H{c[2]}d{c[3]}bs{c[4]}L{c[5]}-{c[6]}k{c[7]}" for c in STREAM_CASES])
+def test_stream_decode(R, Q, H, d, bs, lo, hi, k_top):
+    inp = W.random_decode(900 + R + Q + H + bs, R, Q, H, d, bs, lo, hi, k_top, w_kind="uniform")
+    _full_check(inp, inp.name)
+
+
 def test_decode_with_mask_and_signed_weights():
     inp = W.random_decode(42, 4, 4, 64, 128, 64, 50, 400, 32, w_kind="signed", mask_kind="bias")
     _full_check(inp, inp.name)
