@@ -288,54 +288,84 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Persistent streaming variant (no mask, block_size >= 4).
+// Persistent producer/consumer variant (no mask, block_size >= 4).
 //
 // One workgroup per compute unit.  The work is the list of (row group, key
 // tile) pairs of all requests, row group by row group; each workgroup takes
 // an equal contiguous share of it, computed in the kernel from seq_lens, so
-// short and long requests balance and no workgroup is idle.  Each workgroup
-// then streams its tiles through a 3-deep LDS ring:
-//  * block ids are fetched three tiles ahead of the keys (4-byte
-//    direct-to-LDS loads into a small per-wave ring), keys two tiles ahead of
-//    the compute
-//    (16-byte direct-to-LDS loads into swizzled rows);
-//  * with one query row per request (split head mapping) the q row of a new
-//    row group is fetched by the same direct-to-LDS loads, in fragment
-//    order, into one of two LDS slots, and copied to registers when the
-//    group's first tile is computed, so the ring never drains at a row-group
-//    boundary; with several rows the q block would not fit next to the ring,
-//    so it is loaded into registers and a new row group waits for the last
-//    tile of the previous one;
-//  * every wave issues the same sequence of loads, so exact vmcnt counts tell
-//    when a tile (and the block ids the next request needs) has arrived;
-//  * scores are staged in LDS and written with coalesced stores at the end
-//    (or when the staging area fills), never between the loads.
+// short and long requests balance and no workgroup is idle.
+//
+// A wave can keep only so many loads in flight; issuing one more stalls it
+// until an earlier one returns, and while it stalls it computes nothing.  So
+// each SIMD runs two waves: a producer that does nothing but issue loads and
+// a consumer that does nothing but compute.
+//  * the four producers fetch block ids three tiles ahead (4-byte
+//    direct-to-LDS loads into a small ring per producer), then each key tile
+//    (16-byte direct-to-LDS loads into swizzled rows of a 3-deep ring, a
+//    quarter of the tile each) and, with one query row per request, the q
+//    row of each new row group (same loads, fragment order, one of two LDS
+//    slots).  A producer issues only direct-to-LDS loads, so exact vmcnt
+//    counts tell when its part of a tile has landed; it then publishes its
+//    count of landed tiles in LDS.
+//  * each consumer waits until every producer has published the tile it
+//    needs, computes its 32-key blocks and writes the scores straight to
+//    memory, then publishes how many tiles it has finished; a producer
+//    reuses a ring slot (or a q slot) only when every consumer is done with
+//    it.
+//  * with several query rows per request and >= 32 heads every consumer owns
+//    one row, with the split head mapping, and loads that row's q into
+//    registers when its row group changes.
 // ---------------------------------------------------------------------------
 
-constexpr int kStreamTK = 128;      // keys per tile
-constexpr int kStreamNBUF = 3;      // key tiles in the LDS ring
-constexpr int kMaxRG = 2048;        // row groups handled in-kernel
-constexpr int kBtLead = 3;          // block ids fetched up to this many tiles ahead of the keys
-constexpr int kBtRing = kBtLead + 3; // block-id ring slots per wave
+constexpr int kPcConsumers = 4;                        // compute waves, one per SIMD
+constexpr int kPcProducers = 4;                        // load waves, one per SIMD
+constexpr int kPcWaves = kPcConsumers + kPcProducers;
+constexpr int kPcThreads = kPcWaves * 64;
+constexpr int kStreamTK = 128;                         // keys per tile
+constexpr int kStreamNBUF = 3;                         // key tiles in the LDS ring
+constexpr int kMaxRG = 2048;                           // row groups handled in-kernel
+constexpr int kBtLead = 3;                             // block ids fetched this many tiles ahead
+constexpr int kBtRing = kBtLead + 3;                   // block-id ring slots
+constexpr int kFlagReady = 12;                         // misc words: tiles landed, per producer
+constexpr int kFlagDone = 16;                          // misc words: tiles done, per consumer
 
-template <int H, int D, bool SPLIT>
+template <int H, int D, bool SPLIT, int NC>
 struct StreamGeo {
     using G = Geo<H, D>;
-    static constexpr int MB = SPLIT ? H / 32 : G::MBLK;     // M-blocks per wave
-    static constexpr int QL = MB * G::KSTEPS;               // 16-byte q fragments per lane
-    static constexpr int STAGE = SPLIT ? 2048 : 4096;       // staged scores (floats)
+    static constexpr int NG = kPcConsumers / NC;               // consumer waves along rows
+    static constexpr int MB = SPLIT ? H / 32 : G::MBLK;        // M-blocks per consumer
+    static constexpr int QL = MB * G::KSTEPS;                  // 16-byte q fragments per lane
+    static constexpr int TPB = SPLIT ? 1 : G::TPB;             // query rows per consumer
+    static constexpr int ROWS = NG * TPB;                      // rows of one row group
+    static constexpr bool QLDS = SPLIT && NG == 1;             // q through the LDS slots
     static constexpr int TILE_BYTES = kStreamTK * G::ROWB;
-    static constexpr int QSLOT = SPLIT ? QL * 1024 : 0;     // bytes of one LDS q slot
+    static constexpr int QSLOT = QLDS ? QL * 1024 : 0;         // bytes of one q slot
+    static constexpr int DPT = kStreamTK * G::CPR / 64 / kPcProducers;  // key loads per producer per tile
+    static constexpr int NBW = kStreamTK / (32 * NC);          // 32-key blocks per consumer per tile
     static constexpr size_t lds_bytes() {
-        return (size_t)kStreamNBUF * TILE_BYTES + 2 * (size_t)QSLOT + 4 * (size_t)STAGE +
-               4 * (2 * (size_t)kMaxRG + 1) + 4 * (size_t)kWaves * kBtRing * 64 + 64;
+        return (size_t)kStreamNBUF * TILE_BYTES + 2 * (size_t)QSLOT + 4 * (2 * (size_t)kMaxRG + 1) +
+               4 * (size_t)kPcProducers * kBtRing * 64 + 128;
     }
 };
 
-static_assert(StreamGeo<64, 128, true>::lds_bytes() <= 160 * 1024, "LDS budget");
-static_assert(StreamGeo<64, 128, false>::lds_bytes() <= 160 * 1024, "LDS budget");
+static_assert(StreamGeo<64, 128, true, 4>::lds_bytes() <= 160 * 1024, "LDS budget");
+static_assert(StreamGeo<64, 128, true, 1>::lds_bytes() <= 160 * 1024, "LDS budget");
 
-// q fragments (A operand) of a row group of the general mapping: rows
+// q fragments (A operand) of one query row t with the split head mapping:
+// row m of M-block mb is head (m>>2 & 1)*H/2 + (m>>3)*4 + (m&3) + 16*mb.
+template <int H, int D, int MB, int KS>
+__device__ __forceinline__ void load_q_split(half8 (&qa)[MB][KS], const _Float16 *qp, int64_t q_st,
+                                             int64_t q_sh, int t, int m, int kh) {
+    const int head0 = ((m >> 2) & 1) * (H / 2) + (m >> 3) * 4 + (m & 3);
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+        const _Float16 *src = qp + (int64_t)t * q_st + (int64_t)(head0 + mb * 16) * q_sh + kh * (D / 2);
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk) qa[mb][kk] = *reinterpret_cast<const half8 *>(src + kk * 8);
+    }
+}
+
+// q fragments of the general mapping for consumer tg of a row group: rows
 // row0.. (rhi exclusive).  Rows past rhi repeat row0; their scores are
 // never kept.
 template <int H, int D, int MB, int KS>
@@ -371,25 +401,22 @@ __device__ __forceinline__ void mfma_keys(f32x16 (&acc)[MB], const half8 (&qa)[M
     }
 }
 
+__device__ __forceinline__ int lds_flag(const lds_i32 *p) { return uni(*(const volatile lds_i32 *)p); }
+__device__ __forceinline__ void set_lds_flag(lds_i32 *p, int v) {
+    asm volatile("" ::: "memory");
+    *(volatile lds_i32 *)p = v;
+}
+
 template <int H, int D, bool SPLIT, int NC>
-__global__ void __launch_bounds__(kThreads, 1) decode_stream_kernel(ScoreArgs args, int n_req) {
+__global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args, int n_req) {
     using G = Geo<H, D>;
-    using SG = StreamGeo<H, D, SPLIT>;
+    using SG = StreamGeo<H, D, SPLIT, NC>;
     constexpr int TK = kStreamTK;
-    constexpr int NG = kWaves / NC;                // waves along rows
-    constexpr int NBW = TK / (32 * NC);            // 32-key blocks per wave per tile
-    constexpr int MB = SG::MB;
-    constexpr int KS = G::KSTEPS;
-    constexpr int TPB = SPLIT ? 1 : G::TPB;
+    constexpr int NBW = SG::NBW, MB = SG::MB, KS = G::KSTEPS, TPB = SG::TPB, ROWS = SG::ROWS;
     constexpr int SLOTS = SPLIT ? 1 : G::SLOTS;
-    constexpr int ROWS = NG * TPB;                 // rows of one row group
-    constexpr int TILE_BYTES = SG::TILE_BYTES;
-    constexpr int DPT = TK * G::CPR / kThreads;    // key loads per thread per tile
-    constexpr int QDMA = SPLIT ? SG::QL / kWaves : 0;  // q loads per wave per row group (LDS)
-    constexpr int QREG = SPLIT ? 0 : SG::QL;           // q loads per lane per row group (registers)
-    constexpr int NST = SG::STAGE / (TK * ROWS);   // tiles per staging flush
-    static_assert(NST >= 1, "staging too small");
-    static_assert(!SPLIT || (NC == kWaves && SG::QL % kWaves == 0), "split mapping");
+    constexpr int TILE_BYTES = SG::TILE_BYTES, DPT = SG::DPT;
+    constexpr bool QLDS = SG::QLDS;
+    static_assert(NBW >= 1, "tile too small");
 
     // plain scalars (no argument struct is captured anywhere)
     const _Float16 *const qp = args.q;
@@ -408,27 +435,31 @@ __global__ void __launch_bounds__(kThreads, 1) decode_stream_kernel(ScoreArgs ar
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     lds_u8 *const smem = (lds_u8 *)smem_raw;
     lds_u8 *const keys = smem;
-    lds_u8 *const qslots = smem + kStreamNBUF * TILE_BYTES;                          // split: 2 slots
-    lds_f32 *const stage = (lds_f32 *)(qslots + 2 * SG::QSLOT);
-    lds_i32 *const pref = (lds_i32 *)(stage + SG::STAGE);                            // [n_rg + 1]
+    lds_u8 *const qslots = smem + kStreamNBUF * TILE_BYTES;                          // QLDS: 2 slots
+    lds_i32 *const pref = (lds_i32 *)(qslots + 2 * SG::QSLOT);                        // [n_rg + 1]
     lds_i32 *const slen = pref + kMaxRG + 1;                                         // [n_req]
-    lds_i32 *const btr = slen + kMaxRG;                                              // [waves][ring][64]
-    lds_i32 *const misc = btr + kWaves * kBtRing * 64;
+    lds_i32 *const btr = slen + kMaxRG;                                              // [producer][ring][64]
+    lds_i32 *const misc = btr + kPcProducers * kBtRing * 64;                         // 32 words
 
-    const int tid = threadIdx.x, wid = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wid = uni(tid >> 6), lane = tid & 63;
     const int m = lane & 31, kh = lane >> 5;
-    const int tg = wid / NC, col = wid - tg * NC;
 
     // ---- 1. tiles per row group and their prefix sum ----------------------
-    for (int r = tid; r < n_req; r += kThreads) slen[r] = max(0, seqp[r]);
+    for (int r = tid; r < n_req; r += kPcThreads) slen[r] = max(0, seqp[r]);
+    if (tid < 32) misc[tid] = 0;
     lds_barrier();
     auto rg_bound = [=](int e) {  // keys visible to any row of row group e
         const int req = e / gpr, sub = e - (e / gpr) * gpr;
         const int jmax = min(Q, (sub + 1) * ROWS) - 1;
         return min(max(slen[req] - Q + 1 + jmax, 0), n_cols);
     };
+    auto rg_bound_u = [=](int e) {  // the same for a wave-uniform e
+        const int req = e / gpr, sub = e - (e / gpr) * gpr;
+        const int jmax = min(Q, (sub + 1) * ROWS) - 1;
+        return min(max(uni(slen[req]) - Q + 1 + jmax, 0), n_cols);
+    };
     {
-        const int per = (n_rg + kThreads - 1) / kThreads;
+        const int per = (n_rg + kPcThreads - 1) / kPcThreads;
         int local = 0;
         for (int q = 0; q < per; ++q) {
             const int e = tid * per + q;
@@ -442,7 +473,7 @@ __global__ void __launch_bounds__(kThreads, 1) decode_stream_kernel(ScoreArgs ar
         if (lane == 63) misc[wid] = incl;
         lds_barrier();
         int run = incl - local, total = 0;
-        for (int w = 0; w < kWaves; ++w) {
+        for (int w = 0; w < kPcWaves; ++w) {
             run += w < wid ? misc[w] : 0;
             total += misc[w];
         }
@@ -456,15 +487,15 @@ __global__ void __launch_bounds__(kThreads, 1) decode_stream_kernel(ScoreArgs ar
         if (tid == 0) pref[n_rg] = total;
         lds_barrier();
     }
-    const int64_t T = pref[n_rg];
+    const int64_t T = uni(pref[n_rg]);
     const int t_begin = (int)(T * blockIdx.x / gridDim.x);
     const int t_end = (int)(T * (blockIdx.x + 1) / gridDim.x);
     const int n_mine = t_end - t_begin;
     if (n_mine > 0)
-        for (int e = tid; e < n_rg; e += kThreads)
+        for (int e = tid; e < n_rg; e += kPcThreads)
             if (pref[e] <= t_begin && t_begin < pref[e + 1]) misc[8] = e;
     lds_barrier();
-    const int rg_first = n_mine > 0 ? misc[8] : 0;
+    const int rg_first = n_mine > 0 ? uni(misc[8]) : 0;
 
     // per-tile cursor (wave-uniform): row group, its ordinal among this
     // workgroup's row groups, first key, keys visible to the group
@@ -473,220 +504,217 @@ __global__ void __launch_bounds__(kThreads, 1) decode_stream_kernel(ScoreArgs ar
     do {                                                     \
         const int t_ = t_begin + (j);                        \
         int e_ = rg;                                         \
-        while (pref[e_ + 1] <= t_) ++e_;                     \
+        while (uni(pref[e_ + 1]) <= t_) ++e_;                \
         ord += e_ != rg ? 1 : 0;                             \
         rg = e_;                                             \
-        s0 = (t_ - pref[e_]) * TK;                           \
-        bound = rg_bound(e_);                                \
+        s0 = (t_ - uni(pref[e_])) * TK;                      \
+        bound = rg_bound_u(e_);                              \
     } while (0)
 
-    // compute cursor (tile i), key cursor (tile next_key), block-id cursor
-    // (tile next_bt)
-    int c_rg = rg_first, c_ord = 0, c_s0 = (t_begin - (n_mine > 0 ? pref[rg_first] : 0)) * TK, c_bd = 0;
-    if (n_mine > 0) c_bd = rg_bound(rg_first);
-    int k_rg = c_rg, k_ord = 0, k_s0 = c_s0, k_bd = c_bd;
-    int b_rg = c_rg, b_ord = 0, b_s0 = c_s0, b_bd = c_bd;
-    int next_key = 0, next_bt = 0, last_ord = -1, q_ord = -1;
+    const int s0_first = (t_begin - (n_mine > 0 ? uni(pref[rg_first]) : 0)) * TK;
+    const int bd_first = n_mine > 0 ? rg_bound_u(rg_first) : 0;
 
-    lds_i32 *const bt_mine = btr + wid * kBtRing * 64;
-    int issued = 0;             // vector-memory instructions issued by this wave
-    int mbt0 = 0, mbt1 = 0, mbt2 = 0, mbt3 = 0;  // `issued` after the block ids of tiles next_key..+3
-    int mk0 = 0, mk1 = 0, mk2 = 0;  // `issued` after the keys of tiles i, i+1, i+2
+    if (wid >= kPcConsumers) {
+        // ================= producers =================
+        // producer p issues loads p, p+4, p+8, ... of every tile
+        const int p = wid - kPcConsumers;
+        lds_i32 *const bt_mine = btr + p * kBtRing * 64;
+        int k_rg = rg_first, k_ord = 0, k_s0 = s0_first, k_bd = bd_first;     // tile j
+        int b_rg = rg_first, b_ord = 0, b_s0 = s0_first, b_bd = bd_first;     // tile next_bt
+        int next_bt = 0, issued = 0;
+        int mbt0 = 0, mbt1 = 0, mbt2 = 0, mbt3 = 0;  // `issued` after the block ids of tiles j..j+3
+        int last_ord = -1, gf1 = -1, gf2 = -1, mk_prev = 0;
 
-    half8 qa[MB][KS];
+        // One 16-byte-per-lane load covers KPI consecutive keys (lane l: key
+        // l / CPR, chunk l % CPR).  When the block size is a multiple of KPI
+        // those keys always share a cache block, so a load's address is a
+        // wave-uniform row address plus a lane offset that depends only on
+        // the load index modulo NPAT (the swizzle's period).
+        constexpr int KPI = 64 / G::CPR;
+        constexpr int NPAT = (G::CPR * G::ROWS_PER_256B) / KPI;
+        static_assert(NPAT >= 1 && NPAT <= 4, "swizzle period");
+        const bool kpi_blocks = bs % KPI == 0;
+        // load g = it*4 + p covers keys g*KPI..; with 4*KPI a multiple of the
+        // swizzle period every load of this producer has the same lane offset
+        static_assert((kPcProducers * KPI) % (NPAT * KPI) == 0, "swizzle period");
+        const unsigned lane_off = (unsigned)(((lane / G::CPR) * k_ss +
+                                              (((lane & (G::CPR - 1)) ^ swz<D>(p * KPI + lane / G::CPR)) * 8)) * 2);
 
-    const_f32 *wc = (const_f32 *)wp;
-    float wv[SPLIT ? MB : 1][16];
-    if constexpr (SPLIT) {
-#pragma unroll
-        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) wv[mb][r] = kh ? wc[H / 2 + mb * 16 + r] : wc[mb * 16 + r];
-    }
-
-    int staged = 0, stage_first = 0;
-
-    // block ids of tiles next_bt.. up to next_key+kBtLead, one 4-byte load per lane
-#define LIDX_ISSUE_BT()                                                                                  \
-    while (next_bt < n_mine && next_bt <= next_key + kBtLead) {                                          \
-        const int b0 = sh >= 0 ? b_s0 >> sh : b_s0 / bs;                                                 \
-        const int b_last = sh >= 0 ? (b_s0 + TK - 1) >> sh : (b_s0 + TK - 1) / bs;                       \
-        const int b_used = sh >= 0 ? (b_bd - 1) >> sh : (b_bd - 1) / bs;                                 \
-        const int b = min(min(b0 + lane, b_last), b_used);                                               \
-        dma4(btab + (int64_t)(b_rg / gpr) * bt_stride + b, bt_mine + (next_bt % kBtRing) * 64);          \
-        ++issued;                                                                                        \
-        const int o_ = next_bt - next_key;                                                               \
-        if (o_ == 0) mbt0 = issued;                                                                      \
-        else if (o_ == 1) mbt1 = issued;                                                                 \
-        else if (o_ == 2) mbt2 = issued;                                                                 \
-        else mbt3 = issued;                                                                              \
-        ++next_bt;                                                                                       \
-        if (next_bt < n_mine) LIDX_ADVANCE(b_rg, b_ord, b_s0, b_bd, next_bt);                            \
-    }
-
-    // the first row group's q (general mapping) and the first block ids are
-    // requested together; the compiler-visible wait then covers every load
-    // into registers made before the loop (q, split weights), so that it
-    // inserts no waits of its own inside the loop
-    if constexpr (!SPLIT) {
-        if (n_mine > 0) {
-            const int req_ = rg_first / gpr, sub_ = rg_first - req_ * gpr;
-            const int row0 = req_ * Q + sub_ * ROWS;
-            load_q_rows<H, D, MB, KS>(qa, qp, q_st, q_sh, row0, min(req_ * Q + Q, row0 + ROWS), tg, m, kh);
-            issued += QREG;
-            last_ord = 0;
+#define LIDX_ISSUE_BT(upto)                                                                         \
+        while (next_bt < n_mine && next_bt <= (upto)) {                                             \
+            const int b0 = sh >= 0 ? b_s0 >> sh : b_s0 / bs;                                       \
+            const int b_last = sh >= 0 ? (b_s0 + TK - 1) >> sh : (b_s0 + TK - 1) / bs;             \
+            const int b_used = sh >= 0 ? (b_bd - 1) >> sh : (b_bd - 1) / bs;                       \
+            const int b = min(min(b0 + lane, b_last), b_used);                                     \
+            dma4(btab + (int64_t)(b_rg / gpr) * bt_stride + b, bt_mine + (next_bt % kBtRing) * 64); \
+            ++issued;                                                                              \
+            const int o_ = next_bt - j;                                                            \
+            if (o_ == 0) mbt0 = issued;                                                            \
+            else if (o_ == 1) mbt1 = issued;                                                       \
+            else if (o_ == 2) mbt2 = issued;                                                       \
+            else mbt3 = issued;                                                                    \
+            ++next_bt;                                                                             \
+            if (next_bt < n_mine) LIDX_ADVANCE(b_rg, b_ord, b_s0, b_bd, next_bt);                  \
         }
-    }
-    LIDX_ISSUE_BT();
-    wait_vmem_all_known();
 
-    // step i computes tile i; before that it requests block ids up to two
-    // tiles ahead of the keys and the keys of tile i+2 (the q slots or
-    // registers permitting)
-    for (int i = -2; i < n_mine; ++i) {
-        if (i > 0) LIDX_ADVANCE(c_rg, c_ord, c_s0, c_bd, i);
+        for (int j = 0; j < n_mine; ++j) {
+            if (j > 0) LIDX_ADVANCE(k_rg, k_ord, k_s0, k_bd, j);
+            LIDX_ISSUE_BT(j + kBtLead);
+            wait_vmem_below(issued - mbt0);  // block ids of tile j are in LDS
 
-        // a. block ids of the tiles up to next_key+kBtLead
-        LIDX_ISSUE_BT();
-
-        // b. may the keys of tile next_key be requested now?  (split: the q
-        // slot of row group k_ord last held group k_ord-2, already copied to
-        // registers; otherwise the q registers must be free)
-        const bool req = next_key < n_mine && next_key <= i + 2 &&
-                         k_ord <= max(c_ord, 0) + (SPLIT ? 1 : 0) && next_key < next_bt;
-        int need = -1;
-        if (i >= 0 && next_key > i) need = mk0;      // keys of tile i
-        if (req) need = max(need, mbt0);             // block ids of tile next_key
-        if (need >= 0) wait_vmem_below(issued - need);
-        lds_barrier();  // tile i visible; the slot of tile i-1 (= next_key's) is free
-
-        // c. request the keys of tile next_key (q of its row group first)
-        if (req) {
-            // keys past the group's bound repeat its last visible key (their
-            // scores are discarded), so every address is a used cache slot
-#define LIDX_ISSUE_KEYS()                                                                              \
-    do {                                                                                               \
-        const lds_i32 *bt = bt_mine + (next_key % kBtRing) * 64;                                       \
-        const int b0 = sh >= 0 ? k_s0 >> sh : k_s0 / bs;                                               \
-        lds_u8 *base = keys + (next_key % kStreamNBUF) * TILE_BYTES;                                   \
-        int64_t phys[DPT];                                                                             \
-        _Pragma("unroll") for (int it = 0; it < DPT; ++it) {                                           \
-            const int c = (it * kWaves + wid) * 64 + lane;                                             \
-            const int s = min(k_s0 + c / G::CPR, k_bd - 1);                                           \
-            phys[it] = bt[(sh >= 0 ? s >> sh : s / bs) - b0];                                          \
-        }                                                                                              \
-        _Pragma("unroll") for (int it = 0; it < DPT; ++it) {                                           \
-            const int c = (it * kWaves + wid) * 64 + lane;                                             \
-            const int n = c / G::CPR;                                                                  \
-            const int lc = (c & (G::CPR - 1)) ^ swz<D>(n);                                             \
-            const int s = min(k_s0 + n, k_bd - 1);                                                     \
-            const int slot = sh >= 0 ? (s & (bs - 1)) : s - (s / bs) * bs;                             \
-            dma16(kp + (phys[it] * bs + slot) * k_ss + lc * 8, base + (it * kWaves + wid) * 1024);     \
-        }                                                                                              \
-        issued += DPT;                                                                                 \
-        if (d <= 0) mk0 = issued;                                                                      \
-        else if (d == 1) mk1 = issued;                                                                 \
-        else mk2 = issued;                                                                             \
-        ++next_key;                                                                                    \
-        mbt0 = mbt1;                                                                                   \
-        mbt1 = mbt2;                                                                                   \
-        mbt2 = mbt3;                                                                                   \
-        if (next_key < n_mine) LIDX_ADVANCE(k_rg, k_ord, k_s0, k_bd, next_key);                        \
-    } while (0)
-
-            const int d = next_key - i;
-            const int req_ = k_rg / gpr, sub_ = k_rg - req_ * gpr;
-            const int row0 = req_ * Q + sub_ * ROWS;
-            bool done = false;
-            if constexpr (SPLIT) {
-                if (k_ord != last_ord) {
+            // the ring slot of tile j last held tile j - NBUF; a new row
+            // group's q slot last held the group two back
+            const bool newg = k_ord != last_ord;
+            int need = j - kStreamNBUF + 1;
+            if (QLDS && newg && gf2 >= 0) need = max(need, gf2 + 1);
+            if (need > 0) {
+                for (;;) {
+                    int md = lds_flag(misc + kFlagDone);
+#pragma unroll
+                    for (int w = 1; w < kPcConsumers; ++w) md = min(md, lds_flag(misc + kFlagDone + w));
+                    if (md >= need) break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                asm volatile("" ::: "memory");
+            }
+            if (newg) {
+                if constexpr (QLDS) {
                     // fragment f = mb*KS + kk of lane l at slot + f*1024 + l*16
+                    const int row0 = (k_rg / gpr) * Q + (k_rg - (k_rg / gpr) * gpr) * ROWS;
                     lds_u8 *slot = qslots + (k_ord & 1) * SG::QSLOT;
                     const int head0 = ((m >> 2) & 1) * (H / 2) + (m >> 3) * 4 + (m & 3);
                     const _Float16 *src0 = qp + (int64_t)row0 * q_st + kh * (D / 2);
 #pragma unroll
-                    for (int x = 0; x < QDMA; ++x) {
-                        const int f = x * kWaves + wid, mb = f / KS, kk = f - (f / KS) * KS;
-                        dma16(src0 + (int64_t)(head0 + mb * 16) * q_sh + kk * 8, slot + f * 1024);
+                    for (int x = 0; x < SG::QL / kPcProducers; ++x) {
+                        const int f = x * kPcProducers + p;
+                        dma16(src0 + (int64_t)(head0 + (f / KS) * 16) * q_sh + (f % KS) * 8, slot + f * 1024);
                     }
-                    issued += QDMA;
-                    last_ord = k_ord;
+                    issued += SG::QL / kPcProducers;
                 }
-            } else {
-                if (k_ord != last_ord) {
-                    // general mapping: the q registers were in use until the
-                    // previous step, so this is the deferred tile i itself;
-                    // q and keys are waited for where the compiler sees it
-                    load_q_rows<H, D, MB, KS>(qa, qp, q_st, q_sh, row0, min(req_ * Q + Q, row0 + ROWS), tg, m, kh);
-                    issued += QREG;
-                    last_ord = k_ord;
-                    LIDX_ISSUE_KEYS();
-                    wait_vmem_all_known();
-                    lds_barrier();
-                    done = true;
-                }
+                gf2 = gf1;
+                gf1 = j;
+                last_ord = k_ord;
             }
-            if (!done) {
-                LIDX_ISSUE_KEYS();
-                if (d <= 0) {  // tile i itself had been deferred
-                    wait_vmem_below(issued - mk0);
-                    lds_barrier();
+
+            // keys of tile j; keys past the group's bound repeat its last
+            // visible key (their scores are discarded), so every address is a
+            // used cache slot
+            {
+                const lds_i32 *bt = bt_mine + (j % kBtRing) * 64;
+                const int b0 = sh >= 0 ? k_s0 >> sh : k_s0 / bs;
+                lds_u8 *base = keys + (j % kStreamNBUF) * TILE_BYTES;
+                if (kpi_blocks) {
+                    int sk[DPT], bk[DPT], pk[DPT];
+#pragma unroll
+                    for (int it = 0; it < DPT; ++it) {
+                        int s = k_s0 + (it * kPcProducers + p) * KPI;
+                        if (s >= k_bd) s = (k_bd - 1) & ~(KPI - 1);
+                        sk[it] = s;
+                        bk[it] = sh >= 0 ? s >> sh : s / bs;
+                        pk[it] = bt[bk[it] - b0];
+                    }
+#pragma unroll
+                    for (int it = 0; it < DPT; ++it) {
+                        const int phys = uni(pk[it]);
+                        const char *row = (const char *)(kp + ((int64_t)phys * bs + (sk[it] - bk[it] * bs)) * k_ss);
+                        dma16(row + lane_off, base + (it * kPcProducers + p) * 1024);
+                    }
+                } else {
+#pragma unroll 4
+                    for (int it = 0; it < DPT; ++it) {
+                        const int c = (it * kPcProducers + p) * 64 + lane;
+                        const int n = c / G::CPR;
+                        const int lc = (c & (G::CPR - 1)) ^ swz<D>(n);
+                        const int s = min(k_s0 + n, k_bd - 1);
+                        const int blk = sh >= 0 ? s >> sh : s / bs;
+                        const int64_t phys = bt[blk - b0];
+                        dma16(kp + (phys * bs + (s - blk * bs)) * k_ss + lc * 8, base + (it * kPcProducers + p) * 1024);
+                    }
                 }
+                issued += DPT;
             }
-#undef LIDX_ISSUE_KEYS
+            mbt0 = mbt1;
+            mbt1 = mbt2;
+            mbt2 = mbt3;
+            // tile j-1 (issued one step earlier) is published once it has landed
+            if (j > 0) {
+                wait_vmem_below(issued - mk_prev);
+                if (lane == 0) set_lds_flag(misc + kFlagReady + p, j);
+            }
+            mk_prev = issued;
         }
-
-        if (i >= 0) {
-            if (staged == NST) {
-                // write the staged scores; a full drain keeps stores apart
-                // from the load counting
-                lds_barrier();
-                int e = rg_first;
-                for (int k = 0; k < staged; ++k) {
-                    const int t = t_begin + stage_first + k;
-                    while (pref[e + 1] <= t) ++e;
-                    const int s0k = (t - pref[e]) * TK;
-                    const int req_ = e / gpr, sub_ = e - req_ * gpr;
-                    const int row0 = req_ * Q + sub_ * ROWS;
-                    const int nrows = min(req_ * Q + Q, row0 + ROWS) - row0;
-                    for (int c = tid; c < nrows * TK; c += kThreads) {
-                        const int r = c / TK, x = c - r * TK;
-                        if (s0k + x < n_cols) scorep[(int64_t)(row0 + r) * score_st + s0k + x] = stage[(k * ROWS + r) * TK + x];
-                    }
+        if (n_mine > 0) {
+            wait_vmem_all();
+            if (lane == 0) set_lds_flag(misc + kFlagReady + p, n_mine);
+        }
+#undef LIDX_ISSUE_BT
+        (void)b_ord;
+    } else {
+        // ================= consumers =================
+        const int tg = wid / NC, col = wid - tg * NC;
+        int c_rg = rg_first, c_ord = 0, c_s0 = s0_first, c_bd = bd_first, q_ord = -1;
+        half8 qa[MB][KS];
+        const_f32 *wc = (const_f32 *)wp;
+        float wv[SPLIT ? MB : 1][16];
+        if constexpr (SPLIT) {
+#pragma unroll
+            for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    wv[mb][r] = kh ? wc[H / 2 + mb * 16 + r] : wc[mb * 16 + r];
+                    asm volatile("" : "+v"(wv[mb][r]));  // keep in a register, not reloaded per tile
                 }
-                stage_first += staged;
-                staged = 0;
-                wait_vmem_all();
-                lds_barrier();
+        }
+        wait_vmem_all_known();
+        for (int i = 0; i < n_mine; ++i) {
+            if (i > 0) LIDX_ADVANCE(c_rg, c_ord, c_s0, c_bd, i);
+            for (;;) {  // every producer's part of tile i has landed
+                int mr = lds_flag(misc + kFlagReady);
+#pragma unroll
+                for (int w = 1; w < kPcProducers; ++w) mr = min(mr, lds_flag(misc + kFlagReady + w));
+                if (mr > i) break;
+                __builtin_amdgcn_s_sleep(1);
             }
+            asm volatile("" ::: "memory");
 
-            // d. compute tile i: each wave its NBW 32-key blocks
-            if constexpr (SPLIT) {
-                if (c_ord != q_ord) {  // first tile of a row group: q from its LDS slot
+            const int req_c = c_rg / gpr, sub_c = c_rg - req_c * gpr;
+            const int row0 = req_c * Q + sub_c * ROWS;
+            const int rhi = min(req_c * Q + Q, row0 + ROWS);
+            if (c_ord != q_ord) {  // first tile of a row group: its q
+                if constexpr (QLDS) {
                     const lds_u8 *slot = qslots + (c_ord & 1) * SG::QSLOT + lane * 16;
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                         for (int kk = 0; kk < KS; ++kk)
                             qa[mb][kk] = *reinterpret_cast<const lds_half8 *>(slot + (mb * KS + kk) * 1024);
-                    q_ord = c_ord;
+                } else {
+                    if constexpr (SPLIT) {
+                        const int t = row0 + tg < rhi ? row0 + tg : row0;
+                        load_q_split<H, D, MB, KS>(qa, qp, q_st, q_sh, t, m, kh);
+                    } else {
+                        load_q_rows<H, D, MB, KS>(qa, qp, q_st, q_sh, row0, rhi, tg, m, kh);
+                    }
+                    // a wait the compiler sees: otherwise it cannot tell on
+                    // later tiles that q has landed and waits for the score
+                    // stores in between as well
+                    wait_vmem_all_known();
                 }
+                q_ord = c_ord;
             }
-            const int req_c = c_rg / gpr, sub_c = c_rg - req_c * gpr;
-            const int row0 = req_c * Q + sub_c * ROWS;
-            const int rhi = min(req_c * Q + Q, row0 + ROWS);
             const lds_u8 *tbase = keys + (i % kStreamNBUF) * TILE_BYTES;
-            const int sl = slen[req_c];
+            const int sl = uni(slen[req_c]);
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) {
                 const int nloc = (col * NBW + nb) * 32;
                 const int s = c_s0 + nloc + m;
+                int trow[SLOTS];
                 bool vis[SLOTS];
                 bool any = false;
 #pragma unroll
                 for (int j = 0; j < SLOTS; ++j) {
-                    const int t = SPLIT ? row0 : row0 + tg * TPB + 2 * j + kh;
-                    const int ovis = t < rhi ? min(max(sl - Q + 1 + (t - req_c * Q), 0), n_cols) : 0;
+                    trow[j] = SPLIT ? row0 + tg : row0 + tg * TPB + 2 * j + kh;
+                    const int ovis = trow[j] < rhi ? min(max(sl - Q + 1 + (trow[j] - req_c * Q), 0), n_cols) : 0;
                     vis[j] = s < ovis;
                     any |= vis[j];
                 }
@@ -718,51 +746,29 @@ __global__ void __launch_bounds__(kThreads, 1) decode_stream_kernel(ScoreArgs ar
                         }
                     }
                 }
-                // stage as [tile][row of the group][key]
 #pragma unroll
                 for (int j = 0; j < SLOTS; ++j) {
-                    const int r = SPLIT ? 0 : tg * TPB + 2 * j + kh;
-                    if (!SPLIT || kh == 0) stage[(staged * ROWS + r) * TK + nloc + m] = res[j];
+                    if ((!SPLIT || kh == 0) && trow[j] < rhi && s < n_cols)
+                        scorep[(int64_t)trow[j] * score_st + s] = res[j];
                 }
             }
-            ++staged;
+            // every LDS read of tile i (and of the q slot) has returned
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+            if (lane == 0) set_lds_flag(misc + kFlagDone + wid, i + 1);
         }
-        mk0 = mk1;  // tile i+1 is computed next
-        mk1 = mk2;
-        mk2 = 0;
+        (void)c_bd;
     }
-#undef LIDX_ISSUE_BT
 #undef LIDX_ADVANCE
-    (void)c_bd;
-    (void)b_ord;
 
-    // ---- 3. write what is staged --------------------------------------------
-    lds_barrier();
-    {
-        int e = rg_first;
-        for (int k = 0; k < staged; ++k) {
-            const int t = t_begin + stage_first + k;
-            while (pref[e + 1] <= t) ++e;
-            const int s0k = (t - pref[e]) * TK;
-            const int req_ = e / gpr, sub_ = e - req_ * gpr;
-            const int row0 = req_ * Q + sub_ * ROWS;
-            const int nrows = min(req_ * Q + Q, row0 + ROWS) - row0;
-            for (int c = tid; c < nrows * TK; c += kThreads) {
-                const int r = c / TK, x = c - r * TK;
-                if (s0k + x < n_cols) scorep[(int64_t)(row0 + r) * score_st + s0k + x] = stage[(k * ROWS + r) * TK + x];
-            }
-        }
-    }
-
-    // ---- 4. -inf past the last tile of every row group (shared out) --------
+    // ---- 2. -inf past the last tile of every row group (shared out) --------
     for (int e = blockIdx.x; e < n_rg; e += gridDim.x) {
-        const int lo = (pref[e + 1] - pref[e]) * TK;
+        const int lo = (uni(pref[e + 1]) - uni(pref[e])) * TK;
         if (lo >= n_cols) continue;
         const int req_ = e / gpr, sub_ = e - req_ * gpr;
         const int row0 = req_ * Q + sub_ * ROWS;
         const int nrows = min(req_ * Q + Q, row0 + ROWS) - row0;
         const int width = n_cols - lo;
-        for (int c = tid; c < nrows * width; c += kThreads) {
+        for (int c = tid; c < nrows * width; c += kPcThreads) {
             const int r = c / width;
             scorep[(int64_t)(row0 + r) * score_st + lo + (c - r * width)] = -INFINITY;
         }
@@ -771,28 +777,37 @@ __global__ void __launch_bounds__(kThreads, 1) decode_stream_kernel(ScoreArgs ar
 
 template <int H, int D, bool SPLIT, int NC>
 hipError_t launch_stream(const ScoreArgs &a, int n_req, hipStream_t stream) {
-    auto kern = decode_stream_kernel<H, D, SPLIT, NC>;
-    const size_t bytes = StreamGeo<H, D, SPLIT>::lds_bytes();
+    auto kern = decode_pc_kernel<H, D, SPLIT, NC>;
+    const size_t bytes = StreamGeo<H, D, SPLIT, NC>::lds_bytes();
     static bool attr = false;
     if (!attr) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
         if (e != hipSuccess) return e;
         attr = true;
     }
-    hipLaunchKernelGGL(kern, dim3(device_cu_count()), dim3(kThreads), bytes, stream, a, n_req);
+    hipLaunchKernelGGL(kern, dim3(device_cu_count()), dim3(kPcThreads), bytes, stream, a, n_req);
     return hipGetLastError();
 }
 
 template <int H, int D>
 hipError_t launch_stream_hd(const ScoreArgs &a, const ScorePlan &p, int n_req, hipStream_t stream) {
     if constexpr (H >= 32) {
-        if (p.split) return launch_stream<H, D, true, 4>(a, n_req, stream);
+        if (p.split) {
+            switch (p.nc) {
+                case 4: return launch_stream<H, D, true, 4>(a, n_req, stream);
+                case 2: return launch_stream<H, D, true, 2>(a, n_req, stream);
+                default: return launch_stream<H, D, true, 1>(a, n_req, stream);
+            }
+        }
     }
-    switch (p.nc) {
-        case 4: return launch_stream<H, D, false, 4>(a, n_req, stream);
-        case 2: return launch_stream<H, D, false, 2>(a, n_req, stream);
-        default: return launch_stream<H, D, false, 1>(a, n_req, stream);
+    if constexpr (H < 32) {
+        switch (p.nc) {
+            case 4: return launch_stream<H, D, false, 4>(a, n_req, stream);
+            case 2: return launch_stream<H, D, false, 2>(a, n_req, stream);
+            default: return launch_stream<H, D, false, 1>(a, n_req, stream);
+        }
     }
+    return hipErrorInvalidValue;
 }
 
 template <int H>
@@ -822,6 +837,33 @@ hipError_t launch_h(const ScoreArgs &a, const ScorePlan &p, int D, bool split, h
 ScorePlan plan_decode(ScoreArgs &a, int n_heads, int head_dim, int n_requests) {
     ScorePlan p{};
     const int Q = a.q_per_req;
+    // persistent producer/consumer kernel when its limits hold: every query
+    // row of a request with >= 32 heads gets its own consumer wave (split
+    // head mapping); fewer heads pack 32/heads rows per M-block
+    if (a.mask == nullptr && a.block_size >= 4 && n_requests <= kMaxRG) {
+        const bool split = n_heads >= 32;
+        const int tpb = split ? 1 : 32 / (n_heads < 16 ? n_heads : 16);
+        int ng = 1;
+        while (ng < kPcConsumers && ng * tpb < Q) ng *= 2;
+        const int rows = ng * tpb;
+        const int gpr = (Q + rows - 1) / rows;
+        if ((int64_t)gpr * n_requests <= kMaxRG) {
+            p.stream = true;
+            p.split = split;
+            p.nc = kPcConsumers / ng;
+            p.rows_per_group = rows;
+            p.nbw = kStreamTK / (32 * p.nc);
+            p.tile_keys = kStreamTK;
+            a.nc = p.nc;
+            a.groups_per_req = gpr;
+            a.n_row_groups = gpr * n_requests;
+            a.chunk = kStreamTK;
+            a.n_chunks = 1;
+            p.grid = dim3((unsigned)device_cu_count());
+            return p;
+        }
+    }
+    // chunked kernel: one workgroup per (row group, key chunk)
     const bool split = Q == 1 && n_heads >= 32;
     const int hpb = n_heads < 16 ? n_heads : 16;
     const int tpb = split ? 1 : 32 / hpb;
@@ -834,16 +876,6 @@ ScorePlan plan_decode(ScoreArgs &a, int n_heads, int head_dim, int n_requests) {
     a.nc = p.nc;
     a.groups_per_req = (Q + p.rows_per_group - 1) / p.rows_per_group;
     a.n_row_groups = a.groups_per_req * n_requests;
-    // persistent streaming kernel when its limits hold
-    p.stream = a.mask == nullptr && a.block_size >= 4 && a.n_row_groups <= kMaxRG && n_requests <= kMaxRG;
-    if (p.stream) {
-        p.nbw = kStreamTK / (32 * p.nc);
-        p.tile_keys = kStreamTK;
-        a.chunk = kStreamTK;
-        a.n_chunks = 1;
-        p.grid = dim3((unsigned)device_cu_count());
-        return p;
-    }
     p.nbw = 1;
     p.tile_keys = 32 * p.nc;
     const int max_tiles_lds = kChunkBytes / (p.tile_keys * 2 * head_dim);

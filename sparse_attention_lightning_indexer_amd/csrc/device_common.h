@@ -40,6 +40,11 @@ __device__ __forceinline__ int swz(int n) {
     return (n / Geo<4, D>::ROWS_PER_256B) & (Geo<4, D>::CPR - 1);
 }
 
+// A value the caller knows to be the same in every lane (an LDS word read at
+// a uniform address, say), moved to a scalar register so that the arithmetic
+// and branches that depend on it run on the scalar unit.
+__device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
+
 __device__ __forceinline__ bool half_is_neg_inf(_Float16 h) {
     return __builtin_bit_cast(unsigned short, h) == 0xfc00u;
 }
@@ -77,21 +82,21 @@ __device__ __forceinline__ void lds_barrier() {
 
 // Wait until at most n vector-memory operations of this wave are pending.
 // Loads complete in issue order, so this waits for everything but the n most
-// recent loads.  n is wave-uniform; counts up to 31 are exact (the pipelines
-// here keep fewer than that behind the oldest load they wait for), larger
-// ones are rounded down to 32 or 48 (waiting longer is always safe).
+// recent loads.  n is wave-uniform; every count the 6-bit counter can hold
+// (0..63) is exact, larger ones wait for 63.
 __device__ __forceinline__ void wait_vmem_below(int n) {
 #define LIDX_W(N) \
     case N: asm volatile("s_waitcnt vmcnt(" #N ")" ::: "memory"); break;
-    switch (n < 0 ? 0 : n) {
+    switch (n < 0 ? 0 : (n > 63 ? 63 : n)) {
         LIDX_W(0) LIDX_W(1) LIDX_W(2) LIDX_W(3) LIDX_W(4) LIDX_W(5) LIDX_W(6) LIDX_W(7)
         LIDX_W(8) LIDX_W(9) LIDX_W(10) LIDX_W(11) LIDX_W(12) LIDX_W(13) LIDX_W(14) LIDX_W(15)
         LIDX_W(16) LIDX_W(17) LIDX_W(18) LIDX_W(19) LIDX_W(20) LIDX_W(21) LIDX_W(22) LIDX_W(23)
         LIDX_W(24) LIDX_W(25) LIDX_W(26) LIDX_W(27) LIDX_W(28) LIDX_W(29) LIDX_W(30) LIDX_W(31)
-        default:
-            if (n >= 48) asm volatile("s_waitcnt vmcnt(48)" ::: "memory");
-            else asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
-            break;
+        LIDX_W(32) LIDX_W(33) LIDX_W(34) LIDX_W(35) LIDX_W(36) LIDX_W(37) LIDX_W(38) LIDX_W(39)
+        LIDX_W(40) LIDX_W(41) LIDX_W(42) LIDX_W(43) LIDX_W(44) LIDX_W(45) LIDX_W(46) LIDX_W(47)
+        LIDX_W(48) LIDX_W(49) LIDX_W(50) LIDX_W(51) LIDX_W(52) LIDX_W(53) LIDX_W(54) LIDX_W(55)
+        LIDX_W(56) LIDX_W(57) LIDX_W(58) LIDX_W(59) LIDX_W(60) LIDX_W(61) LIDX_W(62) LIDX_W(63)
+        default: break;
     }
 #undef LIDX_W
 }

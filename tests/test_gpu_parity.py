@@ -148,15 +148,20 @@ def test_decode_wider_rows_than_lengths():
 
 
 def test_paged_equals_contiguous():
-    """The same keys through a permuted block table and contiguously (query
-    j seeing the first P - T + 1 + j keys) give bit-identical scores."""
+    """The same keys through a permuted and an in-order block table give
+    bit-identical scores, and agree with the contiguous layout (query j
+    seeing the first P - T + 1 + j keys) within the score bar."""
     base = W.random_prefill(7, 4, 500, 64, 128, 16, mask_kind="none", w_kind="uniform")
     vis = np.array([500 - 4 + 1 + j for j in range(4)], np.int32)
     contig = dataclasses.replace(base, vis_len=vis)
-    paged = W.paged_from_prefill(base, 64)
+    permuted = W.paged_from_prefill(base, 64)
+    in_order = W.paged_from_prefill(base, 64, permute=False)
     a = gpu_score(contig).cpu().numpy()
-    b = gpu_score(paged).cpu().numpy()
-    assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
+    b = gpu_score(permuted).cpu().numpy()
+    c = gpu_score(in_order).cpu().numpy()
+    assert np.array_equal(b.view(np.uint32), c.view(np.uint32))
+    check_scores(b, oracle.score_inputs(contig), denominators(contig), where="paged vs oracle")
+    check_scores(a, b.astype(np.float64), denominators(contig), where="contiguous vs paged")
 
 
 # ------------------------------------------------------------ metamorphic

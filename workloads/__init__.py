@@ -297,13 +297,15 @@ def random_decode(seed: int, R: int, Q: int, H: int, d: int, block_size: int,
                   max_seq_len=max_seq_len, mask_kind=mask_kind)
 
 
-def paged_from_prefill(inp: PrefillInputs, block_size: int, seed: int = 1) -> DecodeInputs:
-    """Re-lay a one-request prefill case as a paged cache with a seeded block
-    permutation (Q = T, seq_len = P), for layout-equivalence tests."""
+def paged_from_prefill(inp: PrefillInputs, block_size: int, seed: int = 1,
+                       permute: bool = True) -> DecodeInputs:
+    """Re-lay a one-request prefill case as a paged cache (Q = T, seq_len =
+    P), for layout-equivalence tests: blocks placed by a seeded permutation,
+    or in order with `permute=False`."""
     rng = np.random.default_rng(seed)
     P, d = inp.k.shape
     nb = (P + block_size - 1) // block_size
-    perm = rng.permutation(nb + 2).astype(np.int32)
+    perm = (rng.permutation(nb + 2) if permute else np.arange(nb + 2)).astype(np.int32)
     k_cache = np.full((nb + 2, block_size, d), NAN_F16, dtype=F16)
     for b in range(nb):
         rows = inp.k[b * block_size: (b + 1) * block_size]
