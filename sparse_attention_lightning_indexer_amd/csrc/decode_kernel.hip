@@ -704,46 +704,51 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
             }
             const lds_u8 *tbase = keys + (i % kStreamNBUF) * TILE_BYTES;
             const int sl = uni(slen[req_c]);
+            // the products of block nb+1 are issued before the epilogue of
+            // block nb, so the matrix cores and the vector ALUs overlap; keys
+            // past a row's visible length are computed too and masked
+            f32x16 accA[MB], accB[MB];
+            {
+                const int n = col * NBW * 32 + m;
+                mfma_keys<H, D, MB, KS>(accA, qa, tbase + n * G::ROWB, kh, swz<D>(n));
+            }
 #pragma unroll
             for (int nb = 0; nb < NBW; ++nb) {
+                f32x16(&cur)[MB] = (nb & 1) ? accB : accA;
+                f32x16(&nxt)[MB] = (nb & 1) ? accA : accB;
+                if (nb + 1 < NBW) {
+                    const int n = (col * NBW + nb + 1) * 32 + m;
+                    mfma_keys<H, D, MB, KS>(nxt, qa, tbase + n * G::ROWB, kh, swz<D>(n));
+                }
                 const int nloc = (col * NBW + nb) * 32;
                 const int s = c_s0 + nloc + m;
                 int trow[SLOTS];
                 bool vis[SLOTS];
-                bool any = false;
 #pragma unroll
                 for (int j = 0; j < SLOTS; ++j) {
                     trow[j] = SPLIT ? row0 + tg : row0 + tg * TPB + 2 * j + kh;
                     const int ovis = trow[j] < rhi ? min(max(sl - Q + 1 + (trow[j] - req_c * Q), 0), n_cols) : 0;
                     vis[j] = s < ovis;
-                    any |= vis[j];
                 }
                 float res[SLOTS];
+                if constexpr (SPLIT) {
+                    float sum = 0.0f;
 #pragma unroll
-                for (int j = 0; j < SLOTS; ++j) res[j] = -INFINITY;
-                if (__builtin_amdgcn_ballot_w64(any) != 0) {
-                    f32x16 acc[MB];
-                    const int n = nloc + m;
-                    mfma_keys<H, D, MB, KS>(acc, qa, tbase + n * G::ROWB, kh, swz<D>(n));
-                    if constexpr (SPLIT) {
+                    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+                        for (int r = 0; r < 16; ++r) sum = fmaf(relu(cur[mb][r]), wv[mb][r], sum);
+                    sum += __shfl_xor(sum, 32, 64);
+                    res[0] = vis[0] ? sum : -INFINITY;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < SLOTS; ++j) {
                         float sum = 0.0f;
 #pragma unroll
                         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-                            for (int r = 0; r < 16; ++r) sum = fmaf(relu(acc[mb][r]), wv[mb][r], sum);
-                        sum += __shfl_xor(sum, 32, 64);
-                        if (vis[0]) res[0] = sum;
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < SLOTS; ++j) {
-                            float sum = 0.0f;
-#pragma unroll
-                            for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                                for (int rr = 0; rr < 4 * G::G; ++rr)
-                                    sum = fmaf(relu(acc[mb][4 * G::G * j + rr]), wc[mb * G::HPB + rr], sum);
-                            if (vis[j]) res[j] = sum;
-                        }
+                            for (int rr = 0; rr < 4 * G::G; ++rr)
+                                sum = fmaf(relu(cur[mb][4 * G::G * j + rr]), wc[mb * G::HPB + rr], sum);
+                        res[j] = vis[j] ? sum : -INFINITY;
                     }
                 }
 #pragma unroll
