@@ -26,7 +26,6 @@ namespace {
 
 constexpr int kThreads = 1024;
 constexpr int kWaves = kThreads / 64;
-constexpr int kMaxK = 2048;
 constexpr int kBins = 2048;  // widest digit: 11 bits
 constexpr int kDigits = 3;  // bits 31:21, 20:10, 9:0
 __device__ __forceinline__ int digit_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
@@ -389,6 +388,125 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
         mx = max(mx, (uint32_t)sc[8 + 2 * NW + w]);
     }
 
+    int32_t *const idx_out = a.idx + (int64_t)t * a.out_st;
+    float *const val_out = a.val ? a.val + (int64_t)t * a.out_st : nullptr;
+    auto emit = [&](int pos, unsigned long long e) {
+        const int s = (int)(~(uint32_t)(e & 0xffffffffull));
+        idx_out[pos] = s;
+        if (val_out) val_out[pos] = row[s];
+    };
+
+    // ---- fast path: one 12-bit histogram serves as both the select and the
+    // ordering buckets.  Bins are the 12 bits just below the common prefix of
+    // the row's largest and smallest selectable keys.  A descending scan gives
+    // every bin its output offset and finds the bin B holding the last
+    // selected position; keys in higher bins are placed by their rank inside
+    // their bin, the keys of B are ranked among themselves and the best of
+    // them kept (with every key selectable, all bins are taken whole).
+    // Rows with a bin of more than kMaxBucket selected keys, or more than
+    // kMaxCand keys in B, take the general path below instead.
+    {
+        const uint32_t diff = mn ^ mx;
+        const int pos = diff ? 32 - __clz(diff) : 0;
+        if (nsel > 0 && pos > 0) {
+            const int width = pos < 12 ? pos : 12;
+            const int shift = pos - width;
+            const int nb = 1 << width;
+            const bool all0 = nsel <= k;
+            const int sel_total = all0 ? nsel : k;
+#pragma unroll
+            for (int j = 0; j < E; ++j)
+                if (key[j]) atomicAdd(&hist0[(key[j] >> shift) & (nb - 1)], 1u);
+            __syncthreads();
+            // descending exclusive scan of the bin counts
+            constexpr int MAXPER = 4096 / THREADS;
+            const int per = nb > THREADS ? nb / THREADS : 1;
+            int c[MAXPER];
+            int local = 0;
+#pragma unroll
+            for (int q = 0; q < MAXPER; ++q) {
+                c[q] = 0;
+                const int r = tid * per + q;
+                if (q < per && r < nb) {
+                    c[q] = (int)hist0[nb - 1 - r];
+                    local += c[q];
+                }
+            }
+            int total;
+            int run = scan_excl<THREADS>(local, sc + 64, total);
+            int fullmax = 0;  // largest bin taken whole
+#pragma unroll
+            for (int q = 0; q < MAXPER; ++q) {
+                const int r = tid * per + q;
+                if (q < per && r < nb) {
+                    hist1[nb - 1 - r] = (uint32_t)run;  // output offset of the bin
+                    if (run < sel_total && run + c[q] >= sel_total) {
+                        // B: the bin holding the last selected position
+                        sc[0] = nb - 1 - r;
+                        sc[1] = sel_total - run;
+                        sc[2] = c[q];
+                    } else if (run + c[q] <= sel_total) {
+                        fullmax = max(fullmax, c[q]);  // a bin above B, taken whole
+                    }
+                }
+                run += c[q];
+            }
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) fullmax = max(fullmax, __shfl_xor(fullmax, o, 64));
+            if (lane == 0) sc[8 + wid] = fullmax;
+            if (tid == 0) sc[3] = 0;  // keys gathered from bin B
+            __syncthreads();
+            int bmax = 0;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) bmax = max(bmax, sc[8 + w]);
+            // every thread has read sc[8..]; B and its counts stay in sc[0..2]
+            const int B = all0 ? -1 : sc[0];
+            const int need_b = all0 ? 0 : sc[1];
+            const int cnt_b = all0 ? 0 : sc[2];
+            const int kMaxCand = p2 < 512 ? p2 : 512;
+            if (bmax <= kMaxBucket && cnt_b <= kMaxCand) {
+                const int start_b = sel_total - need_b;
+                // scatter: whole bins into their ranges, B's keys to tmp[]
+#pragma unroll
+                for (int j = 0; j < E; ++j) {
+                    const uint32_t u = key[j];
+                    if (!u) continue;
+                    const int d = (int)((u >> shift) & (nb - 1));
+                    const unsigned long long e =
+                        ((unsigned long long)u << 32) | (uint32_t)(~(uint32_t)(tid + THREADS * j));
+                    if (d > B) sel[atomicAdd(&hist1[d], 1u)] = e;
+                    else if (d == B) tmp[atomicAdd((uint32_t *)&sc[3], 1u)] = e;
+                }
+                for (int j = sel_total + tid; j < k; j += THREADS) {
+                    idx_out[j] = -1;
+                    if (val_out) val_out[j] = -INFINITY;
+                }
+                __syncthreads();
+                // whole bins: position = bin start + rank inside the bin
+                for (int j = tid; j < start_b; j += THREADS) {
+                    const unsigned long long e = sel[j];
+                    const uint32_t d = (uint32_t)(e >> (32 + shift)) & (nb - 1);
+                    const int cnt = (int)hist0[d];
+                    const int s0 = (int)hist1[d] - cnt;
+                    int rank = 0;
+                    for (int q = 0; q < cnt; ++q) rank += sel[s0 + q] > e;
+                    emit(s0 + rank, e);
+                }
+                // the partial bin: rank among its keys, keep the best need_b
+                for (int j = tid; j < cnt_b; j += THREADS) {
+                    const unsigned long long e = tmp[j];
+                    int rank = 0;
+                    for (int q = 0; q < cnt_b; ++q) rank += tmp[q] > e;
+                    if (rank < need_b) emit(start_b + rank, e);
+                }
+                return;
+            }
+            // general path: clear what the fast path used
+            for (int i = tid; i < 4096; i += THREADS) hist0[i] = 0u;
+            __syncthreads();
+        }
+    }
+
     // ---- adaptive radix select -----------------------------------------
     const bool all = nsel <= k;
     uint32_t prefix = 0u, pmask = 0u;
@@ -484,13 +602,6 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
     }
     __syncthreads();
 
-    int32_t *idx_out = a.idx + (int64_t)t * a.out_st;
-    float *val_out = a.val ? a.val + (int64_t)t * a.out_st : nullptr;
-    auto emit = [&](int pos, unsigned long long e) {
-        const int s = (int)(~(uint32_t)(e & 0xffffffffull));
-        idx_out[pos] = s;
-        if (val_out) val_out[pos] = row[s];
-    };
     for (int j = total_sel + tid; j < k; j += THREADS) {
         idx_out[j] = -1;
         if (val_out) val_out[j] = -INFINITY;

@@ -232,6 +232,24 @@ def test_topk_row_lengths(n_cols):
         check_topk_exact(gi, gv, s, k, where=f"n_cols={n_cols} k={k}")
 
 
+@pytest.mark.parametrize("n_rows", [4, 520])
+def test_topk_selection_ends_at_a_bin_edge(n_rows):
+    """Rows whose best keys fill the top histogram bins exactly (k = 8, 15),
+    or stop inside a bin of equal keys (k = 10), on the one-row-per-1024-
+    threads and the two-rows-per-CU launch shapes."""
+    rng = np.random.default_rng(5)
+    n = 3000
+    s = rng.uniform(1.0, 2.0, size=(n_rows, n)).astype(np.float32)
+    for r in range(n_rows):
+        pos = rng.permutation(n)[:15]
+        s[r, pos[:3]] = 100.0
+        s[r, pos[3:8]] = 50.0
+        s[r, pos[8:15]] = 25.0
+    for k in (8, 10, 15, 16):
+        gi, gv = gpu_topk(dev(s), k)
+        check_topk_exact(gi, gv, s, k, where=f"bin edge rows={n_rows} k={k}")
+
+
 # ------------------------------------------------------------ full workloads
 
 def _sampled_check(inp, rows, where):
