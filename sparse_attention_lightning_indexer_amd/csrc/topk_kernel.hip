@@ -67,13 +67,14 @@ __device__ int block_exclusive_scan(int v, int *tmp, int &total) {
     return off + incl - v;
 }
 
-template <bool ROW_IN_LDS>
-__global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, int k_pad) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+// General row top-k for one row per workgroup of kThreads: radix select over
+// three digits, each pass re-reading the row from memory, then an
+// index-ordered compaction and a bitonic sort.  Slow but unconditional: the
+// fallback of the long-row kernel below.
+__device__ void topk_row_general(const TopkArgs &a, int k_pad, unsigned char *smem) {
     uint32_t *hist = reinterpret_cast<uint32_t *>(smem);
     unsigned long long *sel = reinterpret_cast<unsigned long long *>(smem + kBins * 4);
     int *tmp = reinterpret_cast<int *>(smem + kBins * 4 + (size_t)k_pad * 8);
-    uint32_t *keys = reinterpret_cast<uint32_t *>(smem + kBins * 4 + (size_t)k_pad * 8 + 256);
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int t = blockIdx.x;
@@ -82,13 +83,7 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, int k_pad) {
     if (a.row_len) n = min(max(a.row_len[t], 0), n);
     const int k = a.k_top;
 
-    if constexpr (ROW_IN_LDS) {
-        for (int i = tid; i < n; i += kThreads) keys[i] = order_key(row[i]);
-    }
-    auto key_at = [&](int i) -> uint32_t {
-        if constexpr (ROW_IN_LDS) return keys[i];
-        else return order_key(row[i]);
-    };
+    auto key_at = [&](int i) -> uint32_t { return order_key(row[i]); };
 
     // ---- radix select: V = k-th largest key, `need` keys == V to take ----
     uint32_t prefix = 0, pmask = 0;
@@ -218,6 +213,308 @@ __global__ void __launch_bounds__(kThreads) topk_kernel(TopkArgs a, int k_pad) {
 }
 
 // ---------------------------------------------------------------------------
+// Long rows (more keys than the register-resident kernel holds): one
+// workgroup per row streams the row three times and never orders it there.
+//  1. count and min/max of the selectable keys;
+//  2. a histogram of the 12 bits just below the common prefix of min and
+//     max (which spreads the keys over many bins, so LDS atomics rarely
+//     collide), whose descending scan gives the bin B holding the k-th key;
+//  3. every key of a bin >= B is gathered into LDS (at most k plus the
+//     kLongCand keys of B).
+// The gathered set is then selected and ordered in LDS: a second 12-bit
+// histogram below the set's own common prefix gives every bin its output
+// offset and the bin holding the last selected position; keys of higher bins
+// go to their bin's range and are placed by their rank inside it, keys of
+// that bin are ranked among themselves.  Sets with a bin of more than
+// kMaxBucket selected keys, or more than 512 keys in the boundary bin, are
+// bitonic-sorted instead; rows whose B holds more than kLongCand keys (or
+// whose selectable keys are all equal) use topk_row_general.
+// ---------------------------------------------------------------------------
+
+constexpr int kMaxBucket = 64;     // largest bin ordered by ranking inside it
+constexpr int kLongCand = 4096;
+constexpr int kLongS = 8192;       // gathered-set capacity (a power of two >= k + kLongCand)
+constexpr int kLongCand2 = 512;    // boundary-bin keys ranked directly in the final ordering
+
+size_t long_lds_bytes(int k_pad) {
+    return 32768 + 8 * (size_t)kLongS + 8 * (size_t)k_pad + 8 * (size_t)kLongCand2 + 4 * 128;
+}
+
+// Calls f(index, value) for every key of the row; 16-byte loads, four per
+// thread in flight, when the row is 16-byte aligned.
+template <typename F>
+__device__ __forceinline__ void stream_row(const float *row, int n, F &&f) {
+    const int tid = threadIdx.x;
+    if (((uintptr_t)row & 15) == 0) {
+        const int n4 = n >> 2;
+        const float4 *r4 = reinterpret_cast<const float4 *>(row);
+        int i = tid;
+        for (; i + 3 * kThreads < n4; i += 4 * kThreads) {
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = r4[i + u * kThreads];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int b = (i + u * kThreads) * 4;
+                f(b, v[u].x);
+                f(b + 1, v[u].y);
+                f(b + 2, v[u].z);
+                f(b + 3, v[u].w);
+            }
+        }
+        for (; i < n4; i += kThreads) {
+            const float4 v = r4[i];
+            f(4 * i, v.x);
+            f(4 * i + 1, v.y);
+            f(4 * i + 2, v.z);
+            f(4 * i + 3, v.w);
+        }
+        for (int j = 4 * n4 + tid; j < n; j += kThreads) f(j, row[j]);
+    } else {
+        for (int j = tid; j < n; j += kThreads) f(j, row[j]);
+    }
+}
+
+// Descending exclusive scan of nb <= 4096 bin counts (each thread owns
+// 4096 / kThreads consecutive bins from the top).  Writes every bin's offset
+// to start[] and reports the bin holding position `total_sel - 1` in
+// sc[0..2] (bin, keys to take from it, its count) and, in sc[8 + wave], the
+// largest bin above it.  Ends with a barrier.
+__device__ void scan_bins_desc(const uint32_t *h, uint32_t *start, int nb, int total_sel, int *sc) {
+    constexpr int MAXPER = 4096 / kThreads;
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int per = nb > kThreads ? nb / kThreads : 1;
+    int c[MAXPER];
+    int local = 0;
+#pragma unroll
+    for (int q = 0; q < MAXPER; ++q) {
+        c[q] = 0;
+        const int r = tid * per + q;
+        if (q < per && r < nb) {
+            c[q] = (int)h[nb - 1 - r];
+            local += c[q];
+        }
+    }
+    int total;
+    int run = block_exclusive_scan(local, sc + 64, total);
+    int fullmax = 0;
+#pragma unroll
+    for (int q = 0; q < MAXPER; ++q) {
+        const int r = tid * per + q;
+        if (q < per && r < nb) {
+            start[nb - 1 - r] = (uint32_t)run;
+            if (run < total_sel && run + c[q] >= total_sel) {
+                sc[0] = nb - 1 - r;
+                sc[1] = total_sel - run;
+                sc[2] = c[q];
+            } else if (run + c[q] <= total_sel) {
+                fullmax = max(fullmax, c[q]);
+            }
+        }
+        run += c[q];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) fullmax = max(fullmax, __shfl_xor(fullmax, o, 64));
+    if (lane == 0) sc[8 + wid] = fullmax;
+    __syncthreads();
+}
+
+__global__ void __launch_bounds__(kThreads, 1) topk_long_kernel(TopkArgs a, int k_pad) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint32_t *hist = reinterpret_cast<uint32_t *>(smem);
+    uint32_t *hcur = reinterpret_cast<uint32_t *>(smem + 16384);
+    unsigned long long *S = reinterpret_cast<unsigned long long *>(smem + 32768);
+    unsigned long long *O = S + kLongS;
+    unsigned long long *cand2 = O + k_pad;
+    int *sc = reinterpret_cast<int *>(cand2 + kLongCand2);
+
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const int t = blockIdx.x;
+    const float *row = a.score + (int64_t)t * a.score_st;
+    int n = a.n_cols;
+    if (a.row_len) n = min(max(a.row_len[t], 0), n);
+    const int k = a.k_top;
+    int32_t *const idx_out = a.idx + (int64_t)t * a.out_st;
+    float *const val_out = a.val ? a.val + (int64_t)t * a.out_st : nullptr;
+    auto emit = [&](int pos, unsigned long long e) {
+        const int s = (int)(~(uint32_t)(e & 0xffffffffull));
+        idx_out[pos] = s;
+        if (val_out) val_out[pos] = row[s];
+    };
+    auto pack = [](int i, uint32_t u) {
+        return ((unsigned long long)u << 32) | (uint32_t)(~(uint32_t)i);
+    };
+
+    // ---- 1. count, min, max -------------------------------------------------
+    int cnt = 0;
+    uint32_t mn = 0xffffffffu, mx = 0u;
+    stream_row(row, n, [&](int, float x) {
+        const uint32_t u = order_key(x);
+        if (u) {
+            ++cnt;
+            mn = min(mn, u);
+            mx = max(mx, u);
+        }
+    });
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        cnt += __shfl_xor(cnt, o, 64);
+        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
+        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
+    }
+    if (lane == 0) {
+        sc[8 + wid] = cnt;
+        sc[8 + kWaves + wid] = (int)mn;
+        sc[8 + 2 * kWaves + wid] = (int)mx;
+    }
+    for (int i = tid; i < 4096; i += kThreads) hist[i] = 0u;
+    if (tid == 0) sc[3] = 0;
+    __syncthreads();
+    int nsel = 0;
+    mn = 0xffffffffu;
+    mx = 0u;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        nsel += sc[8 + w];
+        mn = min(mn, (uint32_t)sc[8 + kWaves + w]);
+        mx = max(mx, (uint32_t)sc[8 + 2 * kWaves + w]);
+    }
+    const bool all = nsel <= k;
+    const int total_sel = all ? nsel : k;
+    for (int j = total_sel + tid; j < k; j += kThreads) {
+        idx_out[j] = -1;
+        if (val_out) val_out[j] = -INFINITY;
+    }
+    if (nsel == 0) return;
+
+    // ---- 2. histogram below the common prefix, boundary bin ----------------
+    int B = -1, shift = 0, nb = 1;
+    if (!all) {
+        const int pos = 32 - __clz(mn ^ mx);
+        if (mn == mx) {  // every selectable key equal: index order decides
+            __syncthreads();
+            topk_row_general(a, k_pad, smem);
+            return;
+        }
+        const int width = pos < 12 ? pos : 12;
+        shift = pos - width;
+        nb = 1 << width;
+        stream_row(row, n, [&](int, float x) {
+            const uint32_t u = order_key(x);
+            if (u) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+        });
+        __syncthreads();
+        scan_bins_desc(hist, hcur, nb, k, sc);
+        B = sc[0];
+        const int cnt_b = sc[2];
+        if (cnt_b > kLongCand) {
+            __syncthreads();
+            topk_row_general(a, k_pad, smem);
+            return;
+        }
+    }
+
+    // ---- 3. gather every key of a bin >= B ----------------------------------
+    stream_row(row, n, [&](int i, float x) {
+        const uint32_t u = order_key(x);
+        if (u && (int)((u >> shift) & (nb - 1)) >= B) S[atomicAdd((uint32_t *)&sc[3], 1u)] = pack(i, u);
+    });
+    __syncthreads();
+    const int m = sc[3];
+
+    // ---- 4. select and order the gathered set ------------------------------
+    uint32_t smn = 0xffffffffu, smx = 0u;
+    for (int q = tid; q < m; q += kThreads) {
+        const uint32_t u = (uint32_t)(S[q] >> 32);
+        smn = min(smn, u);
+        smx = max(smx, u);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        smn = min(smn, (uint32_t)__shfl_xor((int)smn, o, 64));
+        smx = max(smx, (uint32_t)__shfl_xor((int)smx, o, 64));
+    }
+    if (lane == 0) {
+        sc[16 + wid] = (int)smn;
+        sc[16 + kWaves + wid] = (int)smx;
+    }
+    for (int i = tid; i < 4096; i += kThreads) hist[i] = 0u;
+    if (tid == 0) sc[4] = 0;
+    __syncthreads();
+    smn = 0xffffffffu;
+    smx = 0u;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        smn = min(smn, (uint32_t)sc[16 + w]);
+        smx = max(smx, (uint32_t)sc[16 + kWaves + w]);
+    }
+    bool sorted_out = false;
+    if (smn != smx) {
+        const int pos2 = 32 - __clz(smn ^ smx);
+        const int width2 = pos2 < 12 ? pos2 : 12;
+        const int shift2 = pos2 - width2;
+        const int nb2 = 1 << width2;
+        for (int q = tid; q < m; q += kThreads)
+            atomicAdd(&hist[(uint32_t)(S[q] >> (32 + shift2)) & (nb2 - 1)], 1u);
+        __syncthreads();
+        scan_bins_desc(hist, hcur, nb2, total_sel, sc);
+        int bmax = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) bmax = max(bmax, sc[8 + w]);
+        const int B2 = sc[0], need2 = sc[1], cnt2 = sc[2];
+        if (bmax <= kMaxBucket && cnt2 <= kLongCand2) {
+            const int start2 = total_sel - need2;
+            for (int q = tid; q < m; q += kThreads) {
+                const unsigned long long e = S[q];
+                const int d = (int)((uint32_t)(e >> (32 + shift2)) & (nb2 - 1));
+                if (d > B2) O[atomicAdd(&hcur[d], 1u)] = e;
+                else if (d == B2) cand2[atomicAdd((uint32_t *)&sc[4], 1u)] = e;
+            }
+            __syncthreads();
+            for (int j = tid; j < start2; j += kThreads) {
+                const unsigned long long e = O[j];
+                const uint32_t d = (uint32_t)(e >> (32 + shift2)) & (nb2 - 1);
+                const int c = (int)hist[d];
+                const int s0 = (int)hcur[d] - c;
+                int rank = 0;
+                for (int q = 0; q < c; ++q) rank += O[s0 + q] > e;
+                emit(s0 + rank, e);
+            }
+            for (int j = tid; j < cnt2; j += kThreads) {
+                const unsigned long long e = cand2[j];
+                int rank = 0;
+                for (int q = 0; q < cnt2; ++q) rank += cand2[q] > e;
+                if (rank < need2) emit(start2 + rank, e);
+            }
+            sorted_out = true;
+        }
+    }
+    if (!sorted_out) {
+        // bitonic sort of the gathered set, descending
+        int P2 = 1;
+        while (P2 < m) P2 <<= 1;
+        for (int i = m + tid; i < P2; i += kThreads) S[i] = 0ull;
+        __syncthreads();
+        for (int size = 2; size <= P2; size <<= 1) {
+            for (int stride = size >> 1; stride > 0; stride >>= 1) {
+                for (int q = tid; q < (P2 >> 1); q += kThreads) {
+                    const int i = 2 * q - (q & (stride - 1));
+                    const int l = i + stride;
+                    const unsigned long long x = S[i], y = S[l];
+                    const bool desc = (i & size) == 0;
+                    if (desc ? (x < y) : (x > y)) {
+                        S[i] = y;
+                        S[l] = x;
+                    }
+                }
+                __syncthreads();
+            }
+        }
+        for (int j = tid; j < total_sel; j += kThreads) emit(j, S[j]);
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Register-resident variant for rows of up to THREADS*E keys.
 //
 //  * Each thread holds E keys, striped (key t + THREADS*j): coalesced loads,
@@ -246,7 +543,6 @@ hipError_t allow_lds(K kern, size_t bytes) {
     return e;
 }
 
-constexpr int kMaxBucket = 64;
 
 template <int THREADS>
 __device__ __forceinline__ int scan_excl(int v, int *tmp, int &total) {
@@ -711,9 +1007,6 @@ hipError_t launch_rows(const TopkArgs &a, int k_pad, hipStream_t stream) {
     return hipGetLastError();
 }
 
-size_t lds_bytes(int n_cols, int k_pad, bool row_in_lds) {
-    return (size_t)kBins * 4 + (size_t)k_pad * 8 + 256 + (row_in_lds ? (size_t)n_cols * 4 : 0);
-}
 
 
 }  // namespace
@@ -741,11 +1034,10 @@ hipError_t launch_topk(const TopkArgs &a, void *, hipStream_t stream) {
         if (n <= 8192) return launch_rows<1024, 8>(a, k_pad, stream);
         return launch_rows<1024, 16>(a, k_pad, stream);
     }
-    const size_t streamed = lds_bytes(a.n_cols, k_pad, false);
-    auto kern = topk_kernel<false>;
-    hipError_t e = allow_lds(kern, streamed);
+    const size_t bytes = long_lds_bytes(k_pad);
+    hipError_t e = allow_lds(topk_long_kernel, bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, dim3(a.n_rows), dim3(kThreads), streamed, stream, a, k_pad);
+    hipLaunchKernelGGL(topk_long_kernel, dim3(a.n_rows), dim3(kThreads), bytes, stream, a, k_pad);
     return hipGetLastError();
 }
 
