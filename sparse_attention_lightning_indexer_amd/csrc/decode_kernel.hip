@@ -288,51 +288,56 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(ScoreArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Persistent producer/consumer variant (no mask, block_size >= 4).
+// Persistent producer/consumer score kernel, for paged keys (decode,
+// speculative decode).
 //
 // One workgroup per compute unit.  The work is the list of (row group, key
-// tile) pairs of all requests, row group by row group; each workgroup takes
-// an equal contiguous share of it, computed in the kernel from seq_lens, so
-// short and long requests balance and no workgroup is idle.
+// tile) pairs of all rows, row group by row group, where a row group's tiles
+// cover the keys visible to any of its rows; each workgroup takes an equal
+// contiguous share of it, computed in the kernel from seq_lens,
+// so short and long rows balance and no workgroup is idle.
 //
 // A wave can keep only so many loads in flight; issuing one more stalls it
 // until an earlier one returns, and while it stalls it computes nothing.  So
-// each SIMD runs two waves: a producer that does nothing but issue loads and
-// a consumer that does nothing but compute.
-//  * the four producers fetch block ids three tiles ahead (4-byte
-//    direct-to-LDS loads into a small ring per producer), then each key tile
-//    (16-byte direct-to-LDS loads into swizzled rows of a 3-deep ring, a
-//    quarter of the tile each) and, with one query row per request, the q
-//    row of each new row group (same loads, fragment order, one of two LDS
-//    slots).  A producer issues only direct-to-LDS loads, so exact vmcnt
-//    counts tell when its part of a tile has landed; it then publishes its
-//    count of landed tiles in LDS.
-//  * each consumer waits until every producer has published the tile it
-//    needs, computes its 32-key blocks and writes the scores straight to
-//    memory, then publishes how many tiles it has finished; a producer
-//    reuses a ring slot (or a q slot) only when every consumer is done with
-//    it.
-//  * with several query rows per request and >= 32 heads every consumer owns
-//    one row, with the split head mapping, and loads that row's q into
-//    registers when its row group changes.
+// the loads and the arithmetic run on different waves:
+//  * four producers (one per SIMD) fetch, for every tile, a quarter of its
+//    keys (16-byte direct-to-LDS loads into swizzled rows of a 3-deep ring),
+//    its f16 mask rows when a mask is given (same loads, into a mask ring)
+//    and the tile's block ids three tiles ahead (4-byte
+//    direct-to-LDS loads into a small ring per producer); with one query row
+//    per request also the q row of each new row group (fragment order, one
+//    of two LDS slots).  A producer issues only direct-to-LDS loads, so
+//    exact vmcnt counts tell when its part of a tile has landed; it then
+//    publishes its count of landed tiles in LDS.
+//  * each consumer (four, one per SIMD) waits
+//    until every producer has published the tile it needs, computes its
+//    32-key blocks and writes the scores straight to memory, then publishes
+//    how many tiles it has finished; a producer reuses a ring slot (or a q
+//    slot) only when every consumer is done with it.  Consumers load from
+//    memory only when their row group changes (q, visible lengths), so the
+//    compiler never has to wait for their score stores.
+//  * with >= 32 heads every consumer owns one query row and uses the split
+//    head mapping (q in 64 registers, two accumulator sets so the products
+//    of one 32-key block overlap the epilogue of the one before); fewer
+//    heads pack 32/heads rows per M-block.
 // ---------------------------------------------------------------------------
 
-constexpr int kPcConsumers = 4;                        // compute waves, one per SIMD
 constexpr int kPcProducers = 4;                        // load waves, one per SIMD
-constexpr int kPcWaves = kPcConsumers + kPcProducers;
-constexpr int kPcThreads = kPcWaves * 64;
 constexpr int kStreamTK = 128;                         // keys per tile
-constexpr int kStreamNBUF = 3;                         // key tiles in the LDS ring
-constexpr int kMaxRG = 2048;                           // row groups handled in-kernel
+constexpr int kStreamNBUF = 3;                         // tiles in the LDS rings
+constexpr int kMaxRG = 1536;                           // row groups handled in-kernel
 constexpr int kBtLead = 3;                             // block ids fetched this many tiles ahead
 constexpr int kBtRing = kBtLead + 3;                   // block-id ring slots
 constexpr int kFlagReady = 12;                         // misc words: tiles landed, per producer
 constexpr int kFlagDone = 16;                          // misc words: tiles done, per consumer
 
+constexpr int kPcConsumers = 4;                        // compute waves, one per SIMD
+
 template <int H, int D, bool SPLIT, int NC>
 struct StreamGeo {
+    static constexpr int NCONS = kPcConsumers;
     using G = Geo<H, D>;
-    static constexpr int NG = kPcConsumers / NC;               // consumer waves along rows
+    static constexpr int NG = NCONS / NC;                      // consumer waves along rows
     static constexpr int MB = SPLIT ? H / 32 : G::MBLK;        // M-blocks per consumer
     static constexpr int QL = MB * G::KSTEPS;                  // 16-byte q fragments per lane
     static constexpr int TPB = SPLIT ? 1 : G::TPB;             // query rows per consumer
@@ -340,16 +345,18 @@ struct StreamGeo {
     static constexpr bool QLDS = SPLIT && NG == 1;             // q through the LDS slots
     static constexpr int TILE_BYTES = kStreamTK * G::ROWB;
     static constexpr int QSLOT = QLDS ? QL * 1024 : 0;         // bytes of one q slot
+    static constexpr int MROWS4 = (ROWS + 3) / 4;              // mask loads per tile (4 rows of 128 keys each)
+    static constexpr int MSLOT = MROWS4 * 1024;                // bytes of one mask slot
     static constexpr int DPT = kStreamTK * G::CPR / 64 / kPcProducers;  // key loads per producer per tile
     static constexpr int NBW = kStreamTK / (32 * NC);          // 32-key blocks per consumer per tile
     static constexpr size_t lds_bytes() {
-        return (size_t)kStreamNBUF * TILE_BYTES + 2 * (size_t)QSLOT + 4 * (2 * (size_t)kMaxRG + 1) +
+        return (size_t)kStreamNBUF * (TILE_BYTES + MSLOT) + 2 * (size_t)QSLOT + 4 * (3 * (size_t)kMaxRG + 1) +
                4 * (size_t)kPcProducers * kBtRing * 64 + 128;
     }
 };
 
 static_assert(StreamGeo<64, 128, true, 4>::lds_bytes() <= 160 * 1024, "LDS budget");
-static_assert(StreamGeo<64, 128, true, 1>::lds_bytes() <= 160 * 1024, "LDS budget");
+static_assert(StreamGeo<4, 128, false, 1>::lds_bytes() <= 160 * 1024, "LDS budget");
 
 // q fragments (A operand) of one query row t with the split head mapping:
 // row m of M-block mb is head (m>>2 & 1)*H/2 + (m>>3)*4 + (m&3) + 16*mb.
@@ -407,16 +414,22 @@ __device__ __forceinline__ void set_lds_flag(lds_i32 *p, int v) {
     *(volatile lds_i32 *)p = v;
 }
 
+typedef __attribute__((address_space(3))) unsigned short lds_u16;
+
 template <int H, int D, bool SPLIT, int NC>
-__global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args, int n_req) {
+__global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_pc_kernel(ScoreArgs args, int n_req) {
     using G = Geo<H, D>;
     using SG = StreamGeo<H, D, SPLIT, NC>;
+    constexpr int NCONS = kPcConsumers;
     constexpr int TK = kStreamTK;
+    constexpr int NT = (NCONS + kPcProducers) * 64;
+    constexpr int NW = NCONS + kPcProducers;
     constexpr int NBW = SG::NBW, MB = SG::MB, KS = G::KSTEPS, TPB = SG::TPB, ROWS = SG::ROWS;
     constexpr int SLOTS = SPLIT ? 1 : G::SLOTS;
     constexpr int TILE_BYTES = SG::TILE_BYTES, DPT = SG::DPT;
     constexpr bool QLDS = SG::QLDS;
     static_assert(NBW >= 1, "tile too small");
+    static_assert(NCONS + kPcProducers <= 16, "flag words");
 
     // plain scalars (no argument struct is captured anywhere)
     const _Float16 *const qp = args.q;
@@ -427,6 +440,8 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
     const int64_t bt_stride = args.bt_stride;
     const int bs = args.block_size, sh = args.bs_shift;
     const int32_t *const seqp = args.seq_lens;
+    const _Float16 *const maskp = args.mask;        // nullable
+    const int64_t mask_st = args.mask_st;
     const float *const wp = args.w;
     float *const scorep = args.score;
     const int64_t score_st = args.score_st;
@@ -435,35 +450,38 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     lds_u8 *const smem = (lds_u8 *)smem_raw;
     lds_u8 *const keys = smem;
-    lds_u8 *const qslots = smem + kStreamNBUF * TILE_BYTES;                          // QLDS: 2 slots
-    lds_i32 *const pref = (lds_i32 *)(qslots + 2 * SG::QSLOT);                        // [n_rg + 1]
-    lds_i32 *const slen = pref + kMaxRG + 1;                                         // [n_req]
-    lds_i32 *const btr = slen + kMaxRG;                                              // [producer][ring][64]
-    lds_i32 *const misc = btr + kPcProducers * kBtRing * 64;                         // 32 words
+    lds_u8 *const mslots = smem + kStreamNBUF * TILE_BYTES;                        // [NBUF][MSLOT]
+    lds_u8 *const qslots = mslots + kStreamNBUF * SG::MSLOT;                       // QLDS: 2 slots
+    lds_i32 *const pref = (lds_i32 *)(qslots + 2 * SG::QSLOT);                     // [n_rg + 1]
+    lds_i32 *const gbd = pref + kMaxRG + 1;                                        // [n_rg] keys visible to the group
+    lds_i32 *const slen = gbd + kMaxRG;                                            // [n_req]
+    lds_i32 *const btr = slen + kMaxRG;                                            // [producer][ring][64]
+    lds_i32 *const misc = btr + kPcProducers * kBtRing * 64;                       // 32 words
 
     const int tid = threadIdx.x, wid = uni(tid >> 6), lane = tid & 63;
     const int m = lane & 31, kh = lane >> 5;
 
-    // ---- 1. tiles per row group and their prefix sum ----------------------
-    for (int r = tid; r < n_req; r += kPcThreads) slen[r] = max(0, seqp[r]);
+    // keys visible to row t = req*Q + j of request req
+    auto row_vis = [=](int req, int t) {
+        return min(max(slen[req] - Q + 1 + (t - req * Q), 0), n_cols);
+    };
+
+    // ---- 1. keys visible to each row group, tiles, prefix sum ------------
+    for (int r = tid; r < n_req; r += NT) slen[r] = max(0, seqp[r]);
     if (tid < 32) misc[tid] = 0;
     lds_barrier();
-    auto rg_bound = [=](int e) {  // keys visible to any row of row group e
+    for (int e = tid; e < n_rg; e += NT) {
         const int req = e / gpr, sub = e - (e / gpr) * gpr;
-        const int jmax = min(Q, (sub + 1) * ROWS) - 1;
-        return min(max(slen[req] - Q + 1 + jmax, 0), n_cols);
-    };
-    auto rg_bound_u = [=](int e) {  // the same for a wave-uniform e
-        const int req = e / gpr, sub = e - (e / gpr) * gpr;
-        const int jmax = min(Q, (sub + 1) * ROWS) - 1;
-        return min(max(uni(slen[req]) - Q + 1 + jmax, 0), n_cols);
-    };
+        const int r0 = req * Q + sub * ROWS, r1 = min(req * Q + Q, r0 + ROWS);
+        gbd[e] = row_vis(req, r1 - 1);
+    }
+    lds_barrier();
     {
-        const int per = (n_rg + kPcThreads - 1) / kPcThreads;
+        const int per = (n_rg + NT - 1) / NT;
         int local = 0;
         for (int q = 0; q < per; ++q) {
             const int e = tid * per + q;
-            if (e < n_rg) local += (rg_bound(e) + TK - 1) / TK;
+            if (e < n_rg) local += (gbd[e] + TK - 1) / TK;
         }
         int incl = local;
         for (int o = 1; o < 64; o <<= 1) {
@@ -473,7 +491,7 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
         if (lane == 63) misc[wid] = incl;
         lds_barrier();
         int run = incl - local, total = 0;
-        for (int w = 0; w < kPcWaves; ++w) {
+        for (int w = 0; w < NW; ++w) {
             run += w < wid ? misc[w] : 0;
             total += misc[w];
         }
@@ -481,7 +499,7 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
             const int e = tid * per + q;
             if (e < n_rg) {
                 pref[e] = run;
-                run += (rg_bound(e) + TK - 1) / TK;
+                run += (gbd[e] + TK - 1) / TK;
             }
         }
         if (tid == 0) pref[n_rg] = total;
@@ -492,7 +510,7 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
     const int t_end = (int)(T * (blockIdx.x + 1) / gridDim.x);
     const int n_mine = t_end - t_begin;
     if (n_mine > 0)
-        for (int e = tid; e < n_rg; e += kPcThreads)
+        for (int e = tid; e < n_rg; e += NT)
             if (pref[e] <= t_begin && t_begin < pref[e + 1]) misc[8] = e;
     lds_barrier();
     const int rg_first = n_mine > 0 ? uni(misc[8]) : 0;
@@ -508,16 +526,16 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
         ord += e_ != rg ? 1 : 0;                             \
         rg = e_;                                             \
         s0 = (t_ - uni(pref[e_])) * TK;                      \
-        bound = rg_bound_u(e_);                              \
+        bound = uni(gbd[e_]);                                \
     } while (0)
 
     const int s0_first = (t_begin - (n_mine > 0 ? uni(pref[rg_first]) : 0)) * TK;
-    const int bd_first = n_mine > 0 ? rg_bound_u(rg_first) : 0;
+    const int bd_first = n_mine > 0 ? uni(gbd[rg_first]) : 0;
 
-    if (wid >= kPcConsumers) {
+    if (wid >= NCONS) {
         // ================= producers =================
         // producer p issues loads p, p+4, p+8, ... of every tile
-        const int p = wid - kPcConsumers;
+        const int p = wid - NCONS;
         lds_i32 *const bt_mine = btr + p * kBtRing * 64;
         int k_rg = rg_first, k_ord = 0, k_s0 = s0_first, k_bd = bd_first;     // tile j
         int b_rg = rg_first, b_ord = 0, b_s0 = s0_first, b_bd = bd_first;     // tile next_bt
@@ -528,15 +546,13 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
         // One 16-byte-per-lane load covers KPI consecutive keys (lane l: key
         // l / CPR, chunk l % CPR).  When the block size is a multiple of KPI
         // those keys always share a cache block, so a load's address is a
-        // wave-uniform row address plus a lane offset that depends only on
-        // the load index modulo NPAT (the swizzle's period).
+        // wave-uniform row address plus a lane offset; load g = it*4 + p covers
+        // keys g*KPI.., and with 4*KPI a multiple of the swizzle period every
+        // load of this producer has the same lane offset.
         constexpr int KPI = 64 / G::CPR;
         constexpr int NPAT = (G::CPR * G::ROWS_PER_256B) / KPI;
-        static_assert(NPAT >= 1 && NPAT <= 4, "swizzle period");
-        const bool kpi_blocks = bs % KPI == 0;
-        // load g = it*4 + p covers keys g*KPI..; with 4*KPI a multiple of the
-        // swizzle period every load of this producer has the same lane offset
         static_assert((kPcProducers * KPI) % (NPAT * KPI) == 0, "swizzle period");
+        const bool kpi_blocks = bs % KPI == 0;
         const unsigned lane_off = (unsigned)(((lane / G::CPR) * k_ss +
                                               (((lane & (G::CPR - 1)) ^ swz<D>(p * KPI + lane / G::CPR)) * 8)) * 2);
 
@@ -571,19 +587,21 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
                 for (;;) {
                     int md = lds_flag(misc + kFlagDone);
 #pragma unroll
-                    for (int w = 1; w < kPcConsumers; ++w) md = min(md, lds_flag(misc + kFlagDone + w));
+                    for (int w = 1; w < NCONS; ++w) md = min(md, lds_flag(misc + kFlagDone + w));
                     if (md >= need) break;
                     __builtin_amdgcn_s_sleep(1);
                 }
                 asm volatile("" ::: "memory");
             }
+            const int req_k = k_rg / gpr;
+            const int row0_k = req_k * Q + (k_rg - req_k * gpr) * ROWS;
+            const int rhi_k = min(req_k * Q + Q, row0_k + ROWS);
             if (newg) {
                 if constexpr (QLDS) {
                     // fragment f = mb*KS + kk of lane l at slot + f*1024 + l*16
-                    const int row0 = (k_rg / gpr) * Q + (k_rg - (k_rg / gpr) * gpr) * ROWS;
                     lds_u8 *slot = qslots + (k_ord & 1) * SG::QSLOT;
                     const int head0 = ((m >> 2) & 1) * (H / 2) + (m >> 3) * 4 + (m & 3);
-                    const _Float16 *src0 = qp + (int64_t)row0 * q_st + kh * (D / 2);
+                    const _Float16 *src0 = qp + (int64_t)row0_k * q_st + kh * (D / 2);
 #pragma unroll
                     for (int x = 0; x < SG::QL / kPcProducers; ++x) {
                         const int f = x * kPcProducers + p;
@@ -598,12 +616,12 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
 
             // keys of tile j; keys past the group's bound repeat its last
             // visible key (their scores are discarded), so every address is a
-            // used cache slot
+            // key that exists
             {
-                const lds_i32 *bt = bt_mine + (j % kBtRing) * 64;
-                const int b0 = sh >= 0 ? k_s0 >> sh : k_s0 / bs;
                 lds_u8 *base = keys + (j % kStreamNBUF) * TILE_BYTES;
                 if (kpi_blocks) {
+                    const lds_i32 *bt = bt_mine + (j % kBtRing) * 64;
+                    const int b0 = sh >= 0 ? k_s0 >> sh : k_s0 / bs;
                     int sk[DPT], bk[DPT], pk[DPT];
 #pragma unroll
                     for (int it = 0; it < DPT; ++it) {
@@ -620,6 +638,8 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
                         dma16(row + lane_off, base + (it * kPcProducers + p) * 1024);
                     }
                 } else {
+                    const lds_i32 *bt = bt_mine + (j % kBtRing) * 64;
+                    const int b0 = sh >= 0 ? k_s0 >> sh : k_s0 / bs;
 #pragma unroll 4
                     for (int it = 0; it < DPT; ++it) {
                         const int c = (it * kPcProducers + p) * 64 + lane;
@@ -632,6 +652,20 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
                     }
                 }
                 issued += DPT;
+            }
+            // mask rows of tile j: load x covers rows 4x..4x+3 (lane l: row
+            // l / 16, keys 8*(l % 16)..), into [row][128 keys] of the slot;
+            // rows past the group repeat its first row, chunks past the last
+            // column repeat the last full chunk (neither is ever used)
+            if (maskp) {
+                lds_u8 *mslot = mslots + (j % kStreamNBUF) * SG::MSLOT;
+                for (int x = p; x < SG::MROWS4; x += kPcProducers) {
+                    const int r = x * 4 + (lane >> 4);
+                    const int t = row0_k + r < rhi_k ? row0_k + r : row0_k;
+                    const int s = min(k_s0 + (lane & 15) * 8, n_cols - 8);  // n_cols is a multiple of 8
+                    dma16(maskp + (int64_t)t * mask_st + s, mslot + x * 1024);
+                    ++issued;
+                }
             }
             mbt0 = mbt1;
             mbt1 = mbt2;
@@ -654,6 +688,7 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
         const int tg = wid / NC, col = wid - tg * NC;
         int c_rg = rg_first, c_ord = 0, c_s0 = s0_first, c_bd = bd_first, q_ord = -1;
         half8 qa[MB][KS];
+        int rvis[SLOTS];  // keys visible to this consumer's rows
         const_f32 *wc = (const_f32 *)wp;
         float wv[SPLIT ? MB : 1][16];
         if constexpr (SPLIT) {
@@ -680,7 +715,10 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
             const int req_c = c_rg / gpr, sub_c = c_rg - req_c * gpr;
             const int row0 = req_c * Q + sub_c * ROWS;
             const int rhi = min(req_c * Q + Q, row0 + ROWS);
-            if (c_ord != q_ord) {  // first tile of a row group: its q
+            int trow[SLOTS];
+#pragma unroll
+            for (int j = 0; j < SLOTS; ++j) trow[j] = SPLIT ? row0 + tg : row0 + tg * TPB + 2 * j + kh;
+            if (c_ord != q_ord) {  // first tile of a row group: its q, its rows' lengths
                 if constexpr (QLDS) {
                     const lds_u8 *slot = qslots + (c_ord & 1) * SG::QSLOT + lane * 16;
 #pragma unroll
@@ -695,66 +733,102 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
                     } else {
                         load_q_rows<H, D, MB, KS>(qa, qp, q_st, q_sh, row0, rhi, tg, m, kh);
                     }
-                    // a wait the compiler sees: otherwise it cannot tell on
-                    // later tiles that q has landed and waits for the score
-                    // stores in between as well
-                    wait_vmem_all_known();
                 }
+#pragma unroll
+                for (int j = 0; j < SLOTS; ++j) {
+                    int v = 0;
+                    if (trow[j] < rhi) {
+                        v = row_vis(req_c, trow[j]);
+                    }
+                    rvis[j] = v;
+                }
+                // a wait the compiler sees: otherwise it cannot tell on later
+                // tiles that q has landed and waits for the score stores too
+                wait_vmem_all_known();
                 q_ord = c_ord;
             }
             const lds_u8 *tbase = keys + (i % kStreamNBUF) * TILE_BYTES;
-            const int sl = uni(slen[req_c]);
-            // the products of block nb+1 are issued before the epilogue of
-            // block nb, so the matrix cores and the vector ALUs overlap; keys
-            // past a row's visible length are computed too and masked
-            f32x16 accA[MB], accB[MB];
-            {
-                const int n = col * NBW * 32 + m;
-                mfma_keys<H, D, MB, KS>(accA, qa, tbase + n * G::ROWB, kh, swz<D>(n));
-            }
-#pragma unroll
-            for (int nb = 0; nb < NBW; ++nb) {
-                f32x16(&cur)[MB] = (nb & 1) ? accB : accA;
-                f32x16(&nxt)[MB] = (nb & 1) ? accA : accB;
-                if (nb + 1 < NBW) {
-                    const int n = (col * NBW + nb + 1) * 32 + m;
-                    mfma_keys<H, D, MB, KS>(nxt, qa, tbase + n * G::ROWB, kh, swz<D>(n));
-                }
+            const lds_u16 *mbase = (const lds_u16 *)(mslots + (i % kStreamNBUF) * SG::MSLOT);
+
+            // visibility, mask, store of the row sums of 32-key block nb
+            auto store_block = [&](const float (&res)[SLOTS], int nb) {
                 const int nloc = (col * NBW + nb) * 32;
                 const int s = c_s0 + nloc + m;
-                int trow[SLOTS];
-                bool vis[SLOTS];
 #pragma unroll
                 for (int j = 0; j < SLOTS; ++j) {
-                    trow[j] = SPLIT ? row0 + tg : row0 + tg * TPB + 2 * j + kh;
-                    const int ovis = trow[j] < rhi ? min(max(sl - Q + 1 + (trow[j] - req_c * Q), 0), n_cols) : 0;
-                    vis[j] = s < ovis;
+                    bool vis = s < rvis[j];
+                    float add = 0.0f;
+                    if (maskp) {
+                        const int r = trow[j] - row0;
+                        const _Float16 mv = __builtin_bit_cast(_Float16, mbase[r * TK + nloc + m]);
+                        vis = vis && !half_is_neg_inf(mv);
+                        add = (float)mv;
+                    }
+                    const float v = vis ? res[j] + add : -INFINITY;
+                    if ((!SPLIT || kh == 0) && trow[j] < rhi && s < n_cols)
+                        scorep[(int64_t)trow[j] * score_st + s] = v;
                 }
-                float res[SLOTS];
-                if constexpr (SPLIT) {
+            };
+
+            if constexpr (SPLIT) {
+                // the products of block nb+1 are issued before the epilogue
+                // of block nb, so the matrix cores and the vector ALUs overlap
+                f32x16 accA[MB], accB[MB];
+                {
+                    const int n = col * NBW * 32 + m;
+                    mfma_keys<H, D, MB, KS>(accA, qa, tbase + n * G::ROWB, kh, swz<D>(n));
+                }
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) {
+                    f32x16(&cur)[MB] = (nb & 1) ? accB : accA;
+                    f32x16(&nxt)[MB] = (nb & 1) ? accA : accB;
+                    if (nb + 1 < NBW) {
+                        const int n = (col * NBW + nb + 1) * 32 + m;
+                        mfma_keys<H, D, MB, KS>(nxt, qa, tbase + n * G::ROWB, kh, swz<D>(n));
+                    }
                     float sum = 0.0f;
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                         for (int r = 0; r < 16; ++r) sum = fmaf(relu(cur[mb][r]), wv[mb][r], sum);
                     sum += __shfl_xor(sum, 32, 64);
-                    res[0] = vis[0] ? sum : -INFINITY;
-                } else {
+                    const float res[SLOTS] = {sum};
+                    store_block(res, nb);
+                }
+            } else {
+                // general mapping (fewer than 32 heads: one M-block of
+                // 32/heads rows).  The products of a 32-key block, K step by
+                // K step:
+                static_assert(MB == 1, "general mapping: fewer than 32 heads");
+                auto mfma_block = [&](f32x16 &acc, int nb) {
+                    const int n = (col * NBW + nb) * 32 + m;
+                    const lds_u8 *rowp = tbase + n * G::ROWB;
+                    const int f = swz<D>(n);
+                    acc = f32x16{};
+#pragma unroll
+                    for (int kk = 0; kk < KS; ++kk) {
+                        const half8 b = *reinterpret_cast<const lds_half8 *>(rowp + (((kh * KS + kk) ^ f) << 4));
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(qa[0][kk], b, acc, 0, 0, 0);
+                    }
+                };
+                // two accumulator sets: block nb+1 is multiplied while block
+                // nb is rectified, weighted and summed over its heads
+                f32x16 accA, accB;
+                mfma_block(accA, 0);
+#pragma unroll
+                for (int nb = 0; nb < NBW; ++nb) {
+                    f32x16 &cur = (nb & 1) ? accB : accA;
+                    f32x16 &nxt = (nb & 1) ? accA : accB;
+                    if (nb + 1 < NBW) mfma_block(nxt, nb + 1);
+                    float res[SLOTS];
 #pragma unroll
                     for (int j = 0; j < SLOTS; ++j) {
-                        float sum = 0.0f;
+                        res[j] = 0.0f;
 #pragma unroll
-                        for (int mb = 0; mb < MB; ++mb)
-#pragma unroll
-                            for (int rr = 0; rr < 4 * G::G; ++rr)
-                                sum = fmaf(relu(cur[mb][4 * G::G * j + rr]), wc[mb * G::HPB + rr], sum);
-                        res[j] = vis[j] ? sum : -INFINITY;
+                        for (int rr = 0; rr < 4 * G::G; ++rr)
+                            res[j] = fmaf(relu(cur[4 * G::G * j + rr]), wc[rr], res[j]);
                     }
-                }
-#pragma unroll
-                for (int j = 0; j < SLOTS; ++j) {
-                    if ((!SPLIT || kh == 0) && trow[j] < rhi && s < n_cols)
-                        scorep[(int64_t)trow[j] * score_st + s] = res[j];
+                    store_block(res, nb);
                 }
             }
             // every LDS read of tile i (and of the q slot) has returned
@@ -773,7 +847,7 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
         const int row0 = req_ * Q + sub_ * ROWS;
         const int nrows = min(req_ * Q + Q, row0 + ROWS) - row0;
         const int width = n_cols - lo;
-        for (int c = tid; c < nrows * width; c += kPcThreads) {
+        for (int c = tid; c < nrows * width; c += NT) {
             const int r = c / width;
             scorep[(int64_t)(row0 + r) * score_st + lo + (c - r * width)] = -INFINITY;
         }
@@ -782,7 +856,7 @@ __global__ void __launch_bounds__(kPcThreads, 1) decode_pc_kernel(ScoreArgs args
 
 template <int H, int D, bool SPLIT, int NC>
 hipError_t launch_stream(const ScoreArgs &a, int n_req, hipStream_t stream) {
-    auto kern = decode_pc_kernel<H, D, SPLIT, NC>;
+    auto kern = stream_pc_kernel<H, D, SPLIT, NC>;
     const size_t bytes = StreamGeo<H, D, SPLIT, NC>::lds_bytes();
     static bool attr = false;
     if (!attr) {
@@ -790,29 +864,25 @@ hipError_t launch_stream(const ScoreArgs &a, int n_req, hipStream_t stream) {
         if (e != hipSuccess) return e;
         attr = true;
     }
-    hipLaunchKernelGGL(kern, dim3(device_cu_count()), dim3(kPcThreads), bytes, stream, a, n_req);
+    hipLaunchKernelGGL(kern, dim3(device_cu_count()), dim3((kPcConsumers + kPcProducers) * 64), bytes, stream, a, n_req);
     return hipGetLastError();
 }
 
 template <int H, int D>
 hipError_t launch_stream_hd(const ScoreArgs &a, const ScorePlan &p, int n_req, hipStream_t stream) {
-    if constexpr (H >= 32) {
-        if (p.split) {
-            switch (p.nc) {
-                case 4: return launch_stream<H, D, true, 4>(a, n_req, stream);
-                case 2: return launch_stream<H, D, true, 2>(a, n_req, stream);
-                default: return launch_stream<H, D, true, 1>(a, n_req, stream);
-            }
+    if constexpr (H >= 32) {  // >= 32 heads: always the split mapping
+        switch (p.nc) {
+            case 4: return launch_stream<H, D, true, 4>(a, n_req, stream);
+            case 2: return launch_stream<H, D, true, 2>(a, n_req, stream);
+            default: return launch_stream<H, D, true, 1>(a, n_req, stream);
         }
-    }
-    if constexpr (H < 32) {
+    } else {
         switch (p.nc) {
             case 4: return launch_stream<H, D, false, 4>(a, n_req, stream);
             case 2: return launch_stream<H, D, false, 2>(a, n_req, stream);
             default: return launch_stream<H, D, false, 1>(a, n_req, stream);
         }
     }
-    return hipErrorInvalidValue;
 }
 
 template <int H>
@@ -845,17 +915,19 @@ ScorePlan plan_decode(ScoreArgs &a, int n_heads, int head_dim, int n_requests) {
     // persistent producer/consumer kernel when its limits hold: every query
     // row of a request with >= 32 heads gets its own consumer wave (split
     // head mapping); fewer heads pack 32/heads rows per M-block
-    if (a.mask == nullptr && a.block_size >= 4 && n_requests <= kMaxRG) {
+    // the mask travels in 8-key (16-byte) chunks: aligned rows, whole chunks
+    const bool mask_ok = a.mask == nullptr || (a.mask_vec && a.n_cols >= 8 && a.n_cols % 8 == 0);
+    if (mask_ok && a.block_size >= 4 && n_requests <= kMaxRG) {
         const bool split = n_heads >= 32;
         const int tpb = split ? 1 : 32 / (n_heads < 16 ? n_heads : 16);
         int ng = 1;
-        while (ng < kPcConsumers && ng * tpb < Q) ng *= 2;
+        while (ng < 4 && ng * tpb < Q) ng *= 2;
         const int rows = ng * tpb;
         const int gpr = (Q + rows - 1) / rows;
         if ((int64_t)gpr * n_requests <= kMaxRG) {
             p.stream = true;
             p.split = split;
-            p.nc = kPcConsumers / ng;
+            p.nc = 4 / ng;
             p.rows_per_group = rows;
             p.nbw = kStreamTK / (32 * p.nc);
             p.tile_keys = kStreamTK;

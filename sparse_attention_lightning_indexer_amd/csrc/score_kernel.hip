@@ -90,39 +90,49 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
     int bound = misc[0];  // no row of this workgroup sees a key >= bound
 
     if (a.mask != nullptr && bound > key_lo) {
-        int last = key_lo;  // 1 + the last visible key seen by this thread
+        // the last visible key: scan windows of 2048 keys from the bound
+        // down and stop at the first window holding any visible entry (for
+        // a causal mask that is the first one)
         const int nrows = row_hi - row_lo;
-        const int span = bound - key_lo;
-        const int nch = (span + 7) >> 3;
-        for (int c = tid; c < nrows * nch; c += kThreads) {
-            const int r = c / nch;
-            const int s = key_lo + (c - r * nch) * 8;
-            const int t = row_lo + r;
-            const int rv = min(row_vis(t), bound);
-            if (s >= rv) continue;
-            const _Float16 *mrow = a.mask + (int64_t)t * a.mask_st;
-            if (a.mask_vec && s + 8 <= a.n_cols) {
-                const uint4 v = *reinterpret_cast<const uint4 *>(mrow + s);
-                const unsigned int wv[4] = {v.x, v.y, v.z, v.w};
+        const int nch = (bound - key_lo + 7) >> 3;  // 8-key chunks
+        constexpr int WCH = 256;                      // chunks per window
+        for (int whi = nch; whi > 0; whi -= WCH) {
+            const int wlo = whi > WCH ? whi - WCH : 0;
+            const int wn = whi - wlo;
+            int last = key_lo;  // 1 + the last visible key seen by this thread
+            for (int c = tid; c < nrows * wn; c += kThreads) {
+                const int r = c / wn;
+                const int s = key_lo + (wlo + (c - r * wn)) * 8;
+                const int t = row_lo + r;
+                const int rv = min(row_vis(t), bound);
+                if (s >= rv) continue;
+                const _Float16 *mrow = a.mask + (int64_t)t * a.mask_st;
+                if (a.mask_vec && s + 8 <= a.n_cols) {
+                    const uint4 v = *reinterpret_cast<const uint4 *>(mrow + s);
+                    const unsigned int wv[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-                for (int e = 7; e >= 0; --e) {
-                    const unsigned int hbits = (wv[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
-                    if (s + e < rv && hbits != 0xfc00u) {
-                        last = max(last, s + e + 1);
-                        break;
+                    for (int e = 7; e >= 0; --e) {
+                        const unsigned int hbits = (wv[e >> 1] >> ((e & 1) * 16)) & 0xffffu;
+                        if (s + e < rv && hbits != 0xfc00u) {
+                            last = max(last, s + e + 1);
+                            break;
+                        }
                     }
-                }
-            } else {
-                for (int e = min(8, rv - s) - 1; e >= 0; --e) {
-                    if (!half_is_neg_inf(mrow[s + e])) {
-                        last = max(last, s + e + 1);
-                        break;
+                } else {
+                    for (int e = min(8, rv - s) - 1; e >= 0; --e) {
+                        if (!half_is_neg_inf(mrow[s + e])) {
+                            last = max(last, s + e + 1);
+                            break;
+                        }
                     }
                 }
             }
+            if (last > key_lo) atomicMax(&misc[1], last);
+            __syncthreads();
+            const bool found = misc[1] > key_lo;
+            __syncthreads();  // every thread has read misc[1] before any later update
+            if (found) break;
         }
-        if (last > key_lo) atomicMax(&misc[1], last);
-        __syncthreads();
         bound = misc[1];
     }
 
@@ -331,8 +341,8 @@ hipError_t allow_lds(K kern, size_t bytes) {
 
 template <int H, int D>
 hipError_t launch_hd(const ScoreArgs &a, const ScorePlan &p, hipStream_t stream) {
-    if (p.nbw == 2) {
-        auto kern = score_kernel<H, D, 2>;
+    if (p.nbw == 4) {
+        auto kern = score_kernel<H, D, 4>;
         hipError_t e = allow_lds(kern, p.lds_bytes);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL(kern, p.grid, dim3(kThreads), p.lds_bytes, stream, a);
@@ -367,7 +377,7 @@ ScorePlan plan_score(ScoreArgs &a, int n_heads, int head_dim) {
     int ng = 1;
     while (ng < kWaves && ng * tpb < rows) ng *= 2;
     p.nc = kWaves / ng;
-    p.nbw = p.nc == 1 ? 2 : 1;
+    p.nbw = p.nc == 1 ? 4 : 1;
     p.tile_keys = 32 * p.nc * p.nbw;
     p.rows_per_group = ng * tpb;
     a.nc = p.nc;

@@ -135,14 +135,16 @@ def tiny(seed: int = 0) -> PrefillInputs:
 def prefill_causal(seed: int = 0, T: int = 8192, H: int = 64, d: int = 128,
                    k_top: int = 2048) -> PrefillInputs:
     """Causal prefill: T tokens against P=T keys, key s visible to token t
-    iff s <= t (f16 0/-inf mask); every head weight 1/sqrt(d)."""
+    iff s <= t (f16 0/-inf mask, and the visible-prefix hint t + 1); every
+    head weight 1/sqrt(d)."""
     rng = np.random.default_rng(seed)
     P = T
     q = _normal_f16(rng, (T, H, d))
     k = _normal_f16(rng, (P, d))
     w = np.full(H, 1.0 / np.sqrt(d), dtype=np.float32)
     mask = _causal_mask(T, P, 0)
-    return PrefillInputs("prefill_causal", q, k, w, mask, None, k_top)
+    vis = np.arange(1, T + 1, dtype=np.int32)          # the optional visible-prefix hint, t + 1
+    return PrefillInputs("prefill_causal", q, k, w, mask, vis, k_top)
 
 
 def long_chunk(seed: int = 0, T: int = 1024, P: int = 131072, H: int = 64,
@@ -155,7 +157,8 @@ def long_chunk(seed: int = 0, T: int = 1024, P: int = 131072, H: int = 64,
     k = _normal_f16(rng, (P, d), std=0.5)
     w = (rng.standard_normal(H, dtype=np.float32) / np.float32(np.sqrt(d))).astype(np.float32)
     mask = _causal_mask(T, P, P - T)
-    return PrefillInputs("long_chunk", q, k, w, mask, None, k_top,
+    vis = np.arange(P - T + 1, P + 1, dtype=np.int32)  # visible prefix of token t: P - T + 1 + t
+    return PrefillInputs("long_chunk", q, k, w, mask, vis, k_top,
                          {"first_pos": P - T})
 
 
