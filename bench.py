@@ -41,6 +41,119 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
 MALL_BYTES = 256 << 20
 
 
+CSRC = os.path.join(ROOT, "sparse_attention_lightning_indexer_amd", "csrc")
+# sources whose change makes a stored byte count stale, per kernel
+KERNEL_SOURCES = {
+    "score": ["decode_kernel.hip", "score_kernel.hip", "device_common.h", "internal.h", "indexer_api.hip"],
+    "topk": ["topk_kernel.hip", "device_common.h", "internal.h", "indexer_api.hip"],
+}
+TRAFFIC_MARK = "traffic-record:"
+
+
+def source_digest(kernel: str) -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_role(name: str):
+    if "stream_pc_kernel" in name or "decode_kernel" in name or "score_kernel" in name:
+        return "score"
+    if "topk" in name:
+        return "topk"
+    return None
+
+
+def traffic_path(config: str) -> str:
+    return os.path.join(ROOT, "profiles", f"{config}_hbm_traffic.md")
+
+
+def stored_traffic(config: str, kernel: str):
+    """HBM bytes per launch of `kernel` on workload `config` from the
+    committed counter summary (FETCH_SIZE + WRITE_SIZE, each scaled by the
+    plain copy's reading), or None when there is none or the kernel's
+    sources have changed since the counters were taken."""
+    try:
+        with open(traffic_path(config)) as f:
+            lines = [ln for ln in f if ln.strip().startswith(TRAFFIC_MARK)]
+    except OSError:
+        return None
+    for ln in lines:
+        rec = json.loads(ln.strip()[len(TRAFFIC_MARK):])
+        if rec.get("kernel") == kernel and rec.get("source") == source_digest(kernel):
+            return rec["bytes_per_launch"]
+    return None
+
+
+def pmc_summary(config: str, fetch_dir: str, write_dir: str, calib_mib: int) -> str:
+    """Markdown summary of two rocprofv3 counter runs of this benchmark
+    (--pmc FETCH_SIZE, then --pmc WRITE_SIZE, both with --calib-copy-mib):
+    per kernel the mean KiB per dispatch, scaled so that the plain copy
+    reads and writes exactly the bytes it moves."""
+    import csv
+    import glob
+
+    def per_kernel(d):
+        out = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for r in csv.DictReader(f):
+                    out.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        return {k: (len(v), sum(v) / len(v)) for k, v in out.items()}
+
+    fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
+    calib_kib = calib_mib * 1024.0
+    # the copy: writes the calibration size and reads a good part of it
+    # (a fill of the same size writes as much but reads almost nothing)
+    copy = min((k for k in write if k in fetch and fetch[k][1] > 0.25 * calib_kib),
+               key=lambda k: abs(write[k][1] - calib_kib))
+    f_scale, w_scale = calib_kib / fetch[copy][1], calib_kib / write[copy][1]
+    lines = [f"| kernel | dispatches | FETCH_SIZE KiB/dispatch | WRITE_SIZE KiB/dispatch | "
+             f"HBM MB/launch (scaled) |", "|---|---|---|---|---|"]
+    records = []
+    for k in sorted(fetch):
+        role = kernel_role(k)
+        if role is None and k != copy:
+            continue
+        n, fk = fetch[k]
+        wk = write.get(k, (0, 0.0))[1]
+        mb = (fk * f_scale + wk * w_scale) * 1024 / 1e6
+        short = k if len(k) < 90 else k[:87] + "..."
+        lines.append(f"| `{short}` | {n} | {fk:.1f} | {wk:.1f} | {mb:.3f} |")
+        if role is not None:
+            records.append({"config": config, "kernel": role, "name": k,
+                            "fetch_bytes": fk * f_scale * 1024, "write_bytes": wk * w_scale * 1024,
+                            "bytes_per_launch": (fk * f_scale + wk * w_scale) * 1024,
+                            "source": source_digest(role)})
+    txt = "\n".join(lines)
+    txt += (f"\n\nCalibration: the plain copy (`{copy[:60]}...`) moves {calib_mib} MiB each way; "
+            f"FETCH_SIZE read {fetch[copy][1]:.1f} KiB for it (scale {f_scale:.4f}), "
+            f"WRITE_SIZE {write[copy][1]:.1f} KiB (scale {w_scale:.4f}).\n\n")
+    txt += "\n".join(TRAFFIC_MARK + " " + json.dumps(r) for r in records) + "\n"
+    return txt
+
+
+def trace_summary(trace_dir: str) -> str:
+    """Markdown table of the kernel statistics of a rocprofv3
+    --kernel-trace --stats run (the *kernel_stats.csv it writes)."""
+    import csv
+    import glob
+    paths = glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)
+    rows = []
+    for path in paths:
+        with open(path) as f:
+            rows += list(csv.DictReader(f))
+    out = ["| kernel | calls | average us | min us | max us | total % |", "|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        name = r["Name"] if len(r["Name"]) < 90 else r["Name"][:87] + "..."
+        out.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | {float(r['Percentage']):.1f} |")
+    return "\n".join(out) + "\n"
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -52,6 +165,14 @@ def parse():
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--out", default=None, help="also append the JSON line to this file")
+    ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
+                    help="print the markdown summary of two rocprofv3 --pmc runs of this benchmark "
+                         "(FETCH_SIZE, WRITE_SIZE) for --config and exit; needs no GPU")
+    ap.add_argument("--trace-summary", metavar="TRACE_DIR", default=None,
+                    help="print the kernel table of a rocprofv3 --kernel-trace --stats run and exit")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="before the warmup, run a plain f32 copy kernel (out = in * 1) over this "
+                         "many MiB three times: the known-size reference for hardware byte counters")
     return ap.parse_args()
 
 
@@ -91,10 +212,15 @@ def score_bytes_decode(inp) -> int:
 
 def main():
     args = parse()
+    if args.trace_summary:
+        print(trace_summary(args.trace_summary))
+        return
+    if args.pmc_summary:
+        print(pmc_summary(args.config, args.pmc_summary[0], args.pmc_summary[1], args.calib_copy_mib or 1024))
+        return
     if args.gpus != 1:
-        print(f"bench.py measures one GPU only: this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}); see DESIGN.md for how the work would shard.",
-              file=sys.stderr)
+        print(f"bench.py measures one GPU only: the indexer has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -149,6 +275,15 @@ def main():
         run_score(copies[i % n_copies])
         run_topk()
 
+    if args.calib_copy_mib > 0:
+        n = args.calib_copy_mib << 18  # f32 elements
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
     # ---- warmup, then the timed region: exactly `steps` steps --------
     for i in range(warmup):
         step(i)
@@ -199,7 +334,14 @@ def main():
         work = n_rows * n_cols * 4 + n_rows * k_top * 8
         roof = dict(bound="hbm", achieved=work / (kms * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    # HBM bytes the hardware counters saw per launch of the same kernel, as a
+    # rate over the same average duration (GB/s, comparable to `achieved`
+    # for an HBM-bound kernel), and per launch
+    tb = stored_traffic(args.config, kern)
+    roof["traffic"] = None if tb is None else tb / (kms * 1e-3) / 1e9
+    roof["traffic_unit"] = "GB/s"
+    roof["traffic_bytes_per_launch"] = tb
+    roof["algorithmic_bytes_per_launch"] = work if roof["bound"] == "hbm" else None
     roof["kernel"] = kern
     roof["kernel_ms"] = kms
 
