@@ -3,16 +3,19 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
-One step is the whole hot path over one batch of synthetic input: the
-indexer score into a [rows, keys] f32 buffer, then the per-row top-k.  The
-timed region is exactly K steps between two synchronisations; inputs are
-resident in HBM before it starts, and several copies of them are rotated so
-that consecutive steps do not hit the 256 MB Infinity Cache.
+One step is the whole hot path over one batch of synthetic input.  Paged
+keys (decode, spec_decode) go through the fused entry point (the score
+kernel into a workspace, then the per-row top-k kernel); contiguous keys run
+the score into a [rows, keys] f32 buffer, then the per-row top-k.  The timed region is exactly K steps
+between two synchronisations; inputs are resident in HBM before it starts,
+and several copies of them are rotated so that consecutive steps do not hit
+the 256 MB Infinity Cache.
 
 Prints ONE JSON line: throughput in visible (token, key) pairs per second,
 the roofline of the dominant kernel (its average duration measured with HIP
-events on the launch stream over its own timed loop), and the CPU oracle
-timed on a bounded sample of the same workload as a baseline.
+events on the launch stream over its own timed loop; also the score and
+top-k kernels on their own), and the CPU oracle timed on a bounded sample of
+the same workload as a baseline.
 
 Workloads (``--config``):
   tiny            16 tokens x 256 keys, 4 heads of 64, top-32
@@ -170,6 +173,8 @@ def parse():
                          "(FETCH_SIZE, WRITE_SIZE) for --config and exit; needs no GPU")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR", default=None,
                     help="print the kernel table of a rocprofv3 --kernel-trace --stats run and exit")
+    ap.add_argument("--no-kernel-split", action="store_true",
+                    help="skip the separate score and top-k timing loops (and the roofline)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="before the warmup, run a plain f32 copy kernel (out = in * 1) over this "
                          "many MiB three times: the known-size reference for hardware byte counters")
@@ -260,6 +265,10 @@ def main():
     score = torch.empty((n_rows, n_cols), dtype=torch.float32, device=dev)
     idx = torch.empty((n_rows, k_top), dtype=torch.int32, device=dev)
     val = torch.empty((n_rows, k_top), dtype=torch.float32, device=dev)
+    ws = None
+    if paged:
+        ws = torch.empty(li.workspace_bytes(li.OP_FUSED_DECODE, n_rows, n_cols, k_top), dtype=torch.uint8,
+                         device=dev)
 
     def run_score(c):
         if paged:
@@ -271,9 +280,20 @@ def main():
     def run_topk():
         li.topk(score, k_top, idx=idx, val=val)
 
+    def run_fused(c):
+        li.score_topk_fused_decode(c["q"], c["k"], shared["bt"], shared["sl"], inp.Q, inp.max_seq_len,
+                                   shared["w"], k_top, c["mask"], workspace=ws, idx=idx, val=val)
+
+    # one step: paged keys through the fused entry point (score kernel into
+    # a workspace, then the top-k kernel), contiguous keys as score then
+    # top-k (what the fused prefill entry point does, with the score rows in
+    # a caller-visible buffer)
     def step(i):
-        run_score(copies[i % n_copies])
-        run_topk()
+        if paged:
+            run_fused(copies[i % n_copies])
+        else:
+            run_score(copies[i % n_copies])
+            run_topk()
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 18  # f32 elements
@@ -298,6 +318,11 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = ev0.elapsed_time(ev1) / steps
 
+    # check the timed outputs once (cheap sanity: every row's first index is a
+    # visible key or -1)
+    first = idx[:, 0].cpu().numpy()
+    assert np.all((first >= -1) & (first < n_cols))
+
     # ---- per-kernel average durations (HIP events, same stream) -------
     def avg_ms(fn):
         for i in range(3):
@@ -311,17 +336,17 @@ def main():
         torch.cuda.synchronize()
         return a.elapsed_time(b) / steps
 
-    score_ms = avg_ms(lambda i: run_score(copies[i % n_copies]))
-    topk_ms = avg_ms(lambda i: run_topk())
-
-    # check the timed outputs once (cheap sanity: every row's first index is a
-    # visible key or -1)
-    first = idx[:, 0].cpu().numpy()
-    assert np.all((first >= -1) & (first < n_cols))
+    kernels = {}
+    if not args.no_kernel_split:
+        kernels["score"] = avg_ms(lambda i: run_score(copies[i % n_copies]))
+        kernels["topk"] = avg_ms(lambda i: run_topk())
 
     # ---- roofline of the dominant kernel --------------------------------
-    if score_ms >= topk_ms:
-        kern, kms = "score", score_ms
+    out_bytes = n_rows * k_top * 8
+    if "score" not in kernels:
+        kern, kms, work, roof = None, None, None, None
+    elif kernels["score"] >= kernels["topk"]:
+        kern, kms = "score", kernels["score"]
         if paged:
             work = score_bytes_decode(inp)
             roof = dict(bound="hbm", achieved=work / (kms * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
@@ -330,20 +355,21 @@ def main():
             roof = dict(bound="mfma", achieved=work / (kms * 1e-3) / 1e12, peak=MFMA_F16_PEAK_TFLOPS,
                         unit="TFLOP/s")
     else:
-        kern, kms = "topk", topk_ms
-        work = n_rows * n_cols * 4 + n_rows * k_top * 8
+        kern, kms = "topk", kernels["topk"]
+        work = n_rows * n_cols * 4 + out_bytes
         roof = dict(bound="hbm", achieved=work / (kms * 1e-3) / 1e9, peak=HBM_PEAK_GBS, unit="GB/s")
-    roof["frac"] = roof["achieved"] / roof["peak"]
-    # HBM bytes the hardware counters saw per launch of the same kernel, as a
-    # rate over the same average duration (GB/s, comparable to `achieved`
-    # for an HBM-bound kernel), and per launch
-    tb = stored_traffic(args.config, kern)
-    roof["traffic"] = None if tb is None else tb / (kms * 1e-3) / 1e9
-    roof["traffic_unit"] = "GB/s"
-    roof["traffic_bytes_per_launch"] = tb
-    roof["algorithmic_bytes_per_launch"] = work if roof["bound"] == "hbm" else None
-    roof["kernel"] = kern
-    roof["kernel_ms"] = kms
+    if roof is not None:
+        roof["frac"] = roof["achieved"] / roof["peak"]
+        # HBM bytes the hardware counters saw per launch of the same kernel,
+        # as a rate over the same average duration (GB/s, comparable to
+        # `achieved` for an HBM-bound kernel), and per launch
+        tb = stored_traffic(args.config, kern)
+        roof["traffic"] = None if tb is None else tb / (kms * 1e-3) / 1e9
+        roof["traffic_unit"] = "GB/s"
+        roof["traffic_bytes_per_launch"] = tb
+        roof["algorithmic_bytes_per_launch"] = work if roof["bound"] == "hbm" else None
+        roof["kernel"] = kern
+        roof["kernel_ms"] = kms
 
     line = {
         "metric": "indexer score+top-k: (token,key) pairs/s; % of MFMA or HBM roofline",
@@ -362,7 +388,7 @@ def main():
                    "head_dim": inp.d, "k_top": k_top, "visible_pairs": pairs,
                    "input_copies": n_copies},
         "roofline": roof,
-        "kernels_ms": {"score": score_ms, "topk": topk_ms},
+        "kernels_ms": kernels,
         "wall_s": wall,
     }
     if not args.no_cpu_baseline:

@@ -274,8 +274,10 @@ def score_topk_fused_prefill(q, k, w, k_top: int, mask=None, vis_len=None,
 
 def score_topk_fused_decode(q, k_cache, block_table, seq_lens, query_len: int,
                             max_seq_len: int, w, k_top: int, mask=None,
-                            with_values: bool = True, workspace=None):
-    """indexer_score_decode + indexer_topk with scores kept in a workspace."""
+                            with_values: bool = True, workspace=None, idx=None, val=None):
+    """indexer_score_decode + indexer_topk with scores kept in a workspace
+    (one launch when the selection runs inside the score kernel).  `idx` /
+    `val` may be given as [rows, k_top] outputs."""
     torch = _torch()
     lib = load_library()
     dev = _q_checks(q, w)
@@ -288,8 +290,16 @@ def score_topk_fused_decode(q, k_cache, block_table, seq_lens, query_len: int,
         _need(mask, "mask", torch.float16, dev, 2)
         if mask.stride(1) != 1 or tuple(mask.shape) != (RQ, max_seq_len):
             raise ValueError("mask must be [R*Q, max_seq_len] with contiguous rows")
-    idx = torch.empty((RQ, k_top), dtype=torch.int32, device=dev)
-    val = torch.empty((RQ, k_top), dtype=torch.float32, device=dev) if with_values else None
+    if idx is None:
+        idx = torch.empty((RQ, k_top), dtype=torch.int32, device=dev)
+    _need(idx, "idx", torch.int32, dev, 2)
+    if val is None and with_values:
+        val = torch.empty((RQ, k_top), dtype=torch.float32, device=dev)
+    if val is not None:
+        _need(val, "val", torch.float32, dev, 2)
+    for o in (idx, val):
+        if o is not None and (tuple(o.shape) != (RQ, k_top) or not o.is_contiguous()):
+            raise ValueError(f"outputs must be contiguous [{RQ}, {k_top}]")
     ws, need = _workspace(OP_FUSED_DECODE, RQ, max_seq_len, k_top, dev, workspace)
     _check(lib.indexer_score_topk_fused_decode(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), bs, k_cache.stride(1),

@@ -125,7 +125,7 @@ STREAM_CASES = [
     (40, 16, 4, 64, 16, 100, 3000, 24),      # 16 rows per group: a flush every 2 tiles
     (60, 9, 64, 128, 64, 9, 2500, 16),       # two row groups per request
     (50, 1, 16, 64, 2, 1, 800, 10),          # block size 2: chunked kernel
-    (2100, 1, 4, 64, 16, 1, 200, 8),         # > 2048 row groups: chunked kernel
+    (2100, 1, 4, 64, 16, 1, 200, 8),         # 2100 row groups: per-group words fill much of the LDS
 ]
 
 
@@ -134,6 +134,33 @@ STREAM_CASES = [
 def test_stream_decode(R, Q, H, d, bs, lo, hi, k_top):
     inp = W.random_decode(900 + R + Q + H + bs, R, Q, H, d, bs, lo, hi, k_top, w_kind="uniform")
     _full_check(inp, inp.name)
+
+
+def test_fused_decode_reuses_workspace():
+    """The fused paged entry point: three calls on one workspace filled with
+    random bytes, with a request that has no key and rows that see none; each
+    result must equal the score kernel + top-k kernel result bit for bit and
+    the oracle's ranking of the GPU's own scores."""
+    torch = pytest.importorskip("torch")
+    a = W.random_decode(77, 40, 2, 64, 128, 64, 1, 3000, 50)
+    sl = a.seq_lens.copy()
+    sl[5], sl[6] = 0, 1
+    a = dataclasses.replace(a, seq_lens=sl)
+    b = W.random_decode(78, 70, 1, 64, 128, 64, 1, 7000, 64)
+    need = max(li.workspace_bytes(li.OP_FUSED_DECODE, x.R * x.Q, x.max_seq_len, x.k_top) for x in (a, b))
+    gen = torch.Generator(device=DEV).manual_seed(5)
+    ws = torch.randint(0, 256, (need,), dtype=torch.uint8, device=DEV, generator=gen)
+    for inp in (a, b, a):
+        fi, fv = li.score_topk_fused_decode(dev(inp.q), dev(inp.k_cache), dev(inp.block_table),
+                                            dev(inp.seq_lens), inp.Q, inp.max_seq_len, dev(inp.w),
+                                            inp.k_top, workspace=ws)
+        torch.cuda.synchronize()
+        fi, fv = fi.cpu().numpy(), fv.cpu().numpy()
+        g_t = gpu_score(inp)
+        gi, gv = gpu_topk(g_t, inp.k_top)
+        assert np.array_equal(fi, gi), f"{inp.name}: fused indices differ"
+        assert np.array_equal(fv.view(np.uint32), gv.view(np.uint32)), f"{inp.name}: values differ"
+        check_topk_exact(fi, fv, g_t.cpu().numpy(), inp.k_top, where=inp.name)
 
 
 def test_decode_with_mask_and_signed_weights():
