@@ -173,6 +173,8 @@ def parse():
                          "(FETCH_SIZE, WRITE_SIZE) for --config and exit; needs no GPU")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR", default=None,
                     help="print the kernel table of a rocprofv3 --kernel-trace --stats run and exit")
+    ap.add_argument("--no-peak-probe", action="store_true",
+                    help="skip the measured-peak probes reported beside the published peak")
     ap.add_argument("--no-kernel-split", action="store_true",
                     help="skip the separate score and top-k timing loops (and the roofline)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -370,6 +372,15 @@ def main():
         roof["algorithmic_bytes_per_launch"] = work if roof["bound"] == "hbm" else None
         roof["kernel"] = kern
         roof["kernel_ms"] = kms
+        if not args.no_peak_probe:
+            # the same kernel against what this device sustains: an LDS-fed
+            # f16 MFMA stream, or a 4 GiB streaming read
+            peaks = li.probe_peaks(dev)
+            measured = peaks["read_gbs"] if roof["bound"] == "hbm" else peaks["mfma_f16_tflops"]
+            roof["measured_peak"] = measured
+            roof["frac_of_measured"] = roof["achieved"] / measured
+            roof["measured_peak_probe"] = ("streaming read of 4 GiB" if roof["bound"] == "hbm" else
+                                           "f16 MFMA 32x32x16, B fragments from LDS, 2 waves per SIMD")
 
     line = {
         "metric": "indexer score+top-k: (token,key) pairs/s; % of MFMA or HBM roofline",

@@ -29,6 +29,7 @@ EXPORTS = (
     "indexer_score_prefill", "indexer_score_decode", "indexer_topk",
     "indexer_score_topk_fused_prefill", "indexer_score_topk_fused_decode",
     "indexer_workspace_bytes",
+    "indexer_probe_sink_floats", "indexer_probe_mfma", "indexer_probe_read",
 )
 
 
@@ -79,6 +80,12 @@ def load_library(path: str = LIB_PATH):
                                                     i32, i32, i32, p, p, i64, i32, i32,
                                                     i32, p, p, i64, p, sz, p]
     lib.indexer_score_topk_fused_decode.restype = st
+    lib.indexer_probe_sink_floats.argtypes = []
+    lib.indexer_probe_sink_floats.restype = i32
+    lib.indexer_probe_mfma.argtypes = [i32, p, p, p]
+    lib.indexer_probe_mfma.restype = st
+    lib.indexer_probe_read.argtypes = [p, sz, p, p]
+    lib.indexer_probe_read.restype = st
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -309,8 +316,42 @@ def score_topk_fused_decode(q, k_cache, block_table, seq_lens, query_len: int,
     return idx, val
 
 
+def probe_peaks(device=None, mfma_iters: int = 4000, read_bytes: int = 4 << 30, repeats: int = 3):
+    """Measured peaks of the device (measurement helpers, not the indexer):
+    sustained f16 MFMA TFLOP/s with B operands from LDS, and streaming-read
+    GB/s over `read_bytes`.  Each is the best of `repeats` timed launches
+    after one untimed launch."""
+    torch = _torch()
+    lib = load_library()
+    dev = device or torch.device("cuda", torch.cuda.current_device())
+    sink = torch.empty(lib.indexer_probe_sink_floats(), dtype=torch.float32, device=dev)
+    buf = torch.empty(read_bytes // 4, dtype=torch.float32, device=dev).fill_(0.0)
+    flops = ctypes.c_double(0.0)
+    s = _stream(dev)
+
+    def timed(fn):
+        fn()
+        best = None
+        for _ in range(repeats):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize(dev)
+            ms = a.elapsed_time(b)
+            best = ms if best is None else min(best, ms)
+        return best
+
+    ms_m = timed(lambda: _check(lib.indexer_probe_mfma(mfma_iters, _ptr(sink), ctypes.byref(flops), s)))
+    ms_r = timed(lambda: _check(lib.indexer_probe_read(_ptr(buf), read_bytes, _ptr(sink), s)))
+    out = {"mfma_f16_tflops": flops.value / (ms_m * 1e-3) / 1e12, "read_gbs": read_bytes / (ms_r * 1e-3) / 1e9,
+           "mfma_ms": ms_m, "read_ms": ms_r}
+    del buf
+    return out
+
+
 __all__ = [
     "score_prefill", "score_decode", "topk", "score_topk_fused_prefill",
     "score_topk_fused_decode", "workspace_bytes", "load_library", "IndexerError",
-    "EXPORTS", "MAX_K_TOP",
+    "EXPORTS", "MAX_K_TOP", "probe_peaks",
 ]

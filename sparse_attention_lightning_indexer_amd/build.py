@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libindexer.so")
-SOURCES = ["indexer_api.hip", "score_kernel.hip", "decode_kernel.hip", "topk_kernel.hip"]
+SOURCES = ["indexer_api.hip", "score_kernel.hip", "decode_kernel.hip", "topk_kernel.hip", "peak_probe.hip"]
 ARCH = os.environ.get("INDEXER_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [

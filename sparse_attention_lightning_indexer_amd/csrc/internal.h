@@ -79,4 +79,10 @@ hipError_t launch_topk(const TopkArgs &a, void *workspace, hipStream_t stream);
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 
+// Achievable-peak probes (peak_probe.hip): an LDS-fed f16 MFMA stream and a
+// streaming read.  `sink` holds probe_sink_floats() floats.
+hipError_t launch_probe_mfma(int iters, float *sink, double *flops, hipStream_t stream);
+hipError_t launch_probe_read(const void *buf, size_t bytes, float *sink, hipStream_t stream);
+int probe_sink_floats();
+
 }  // namespace lidx

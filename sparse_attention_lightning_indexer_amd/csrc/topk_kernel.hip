@@ -3,20 +3,20 @@
 //
 // Order: score descending, equal scores by lower key index; -inf and NaN are
 // never selected; -0 ties with +0; short rows are padded with (-1, -inf).
-//
-// One workgroup (1024 threads) per row:
-//  1. Every score maps to an order-preserving 32-bit key (0 = not
-//     selectable).  Rows that fit in LDS are converted once into LDS; longer
-//     rows are re-read from global memory on each pass.
-//  2. Radix select over three digits (bits 31:21, 20:10, 9:0) with LDS
-//     histograms finds the k-th largest key V and how many keys equal to V
-//     are needed.
-//  3. An index-ordered compaction (wave ballots + a block scan) gathers every
-//     key > V and the lowest-index keys == V, so ties resolve to the lower
-//     index.
-//  4. The selected (key, ~index) pairs are sorted descending by a bitonic
-//     network in LDS and written out; values are re-read from the row so
-//     that they are reported exactly as stored.
+// Every score maps to an order-preserving 32-bit key (0 = not selectable);
+// values are re-read from the row so that they are reported exactly as
+// stored.  Three kernels, by row length:
+//  * rows of up to 16384 keys (topk_rows_kernel): one workgroup per row, the
+//    keys register-resident.  Fast path: one histogram of the 12 bits just
+//    below the common prefix of the row's largest and smallest selectable
+//    keys selects and orders at once (a descending scan gives every bin its
+//    output offset; a key's position is its bin's offset plus its rank inside
+//    the bin).  Crowded bins take an adaptive 12-bit radix select, an
+//    index-ordered compaction and a bucketed or bitonic ordering.
+//  * longer rows (topk_long_kernel): the row is streamed three times to find
+//    the bin of the k-th key and gather the candidates into LDS, which are
+//    then selected and ordered the same way.
+//  * topk_row_general: the fully general streaming fallback (heavy ties).
 #include "internal.h"
 
 #include <math.h>

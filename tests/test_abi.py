@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 12, names  # 9 for the indexer, 3 measurement helpers
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(li.EXPORTS)
@@ -152,3 +152,14 @@ def test_fused_workspace_checks(lib):
     st = lib.indexer_score_topk_fused_decode(A, 64 * 128, 128, B, 64, 128, A, 2, A, 2, 1, 128, A, None, 0,
                                              64, 128, 8, B, None, 8, A, 16, None)
     assert st == li.EWORKSPACE
+
+
+def test_probe_argument_checks(lib):
+    """The measured-peak probes validate before launching (no GPU needed)."""
+    d = ctypes.c_double(0.0)
+    assert lib.indexer_probe_mfma(0, A, ctypes.byref(d), None) == li.EINVAL
+    assert lib.indexer_probe_mfma(10, None, ctypes.byref(d), None) == li.EINVAL
+    assert lib.indexer_probe_read(None, 1 << 20, A, None) == li.EINVAL
+    assert lib.indexer_probe_read(A + 4, 1 << 20, A, None) == li.EINVAL
+    assert lib.indexer_probe_read(A, 17, A, None) == li.EINVAL
+    assert b"multiple of 16" in lib.indexer_last_error()

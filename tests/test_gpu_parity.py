@@ -325,3 +325,11 @@ def test_workload_long_chunk():
     inp = W.long_chunk()
     rows = np.array([0, 1, 511, 1022, 1023])
     _sampled_check(inp, rows, "long_chunk")
+
+
+def test_peak_probes_measure_something():
+    """The measured-peak probes run and report plausible rates (well above a
+    tenth and below twice the published 2.5 PFLOP/s and 8 TB/s)."""
+    r = li.probe_peaks(DEV, mfma_iters=200, read_bytes=256 << 20, repeats=1)
+    assert 250.0 < r["mfma_f16_tflops"] < 5000.0, r
+    assert 800.0 < r["read_gbs"] < 16000.0, r
