@@ -164,6 +164,8 @@ def score_prefill(q, k, w, mask=None, vis_len=None, out=None):
     if out is None:
         out = torch.empty((T, P), dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, dev, 2)
+    if T == 0 or P == 0:  # nothing to compute (and empty tensors have no address)
+        return out
     _check(lib.indexer_score_prefill(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), _ptr(w),
         _ptr(mask), mask.stride(0) if mask is not None else 0, _ptr(vis_len),
@@ -206,6 +208,8 @@ def score_decode(q, k_cache, block_table, seq_lens, query_len: int,
     if out is None:
         out = torch.empty((RQ, max_seq_len), dtype=torch.float32, device=dev)
     _need(out, "out", torch.float32, dev, 2)
+    if RQ == 0 or max_seq_len == 0:  # nothing to compute
+        return out
     _check(lib.indexer_score_decode(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), bs, k_cache.stride(1),
         _ptr(block_table), block_table.stride(0), _ptr(seq_lens), R, query_len,
@@ -236,6 +240,8 @@ def topk(score, k_top: int, row_len=None, with_values: bool = True,
         val = torch.empty((n_rows, k_top), dtype=torch.float32, device=dev)
     ws_n = workspace_bytes(OP_TOPK, n_rows, n_cols, k_top)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev) if ws_n else None
+    if n_rows == 0:  # nothing to select
+        return idx, val
     _check(lib.indexer_topk(
         _ptr(score), score.stride(0), n_rows, n_cols, _ptr(row_len), k_top,
         _ptr(idx), _ptr(val), idx.stride(0), _ptr(ws), ws_n, _stream(dev)))
@@ -270,6 +276,8 @@ def score_topk_fused_prefill(q, k, w, k_top: int, mask=None, vis_len=None,
         vis_len = vis_len.contiguous()
     idx = torch.empty((T, k_top), dtype=torch.int32, device=dev)
     val = torch.empty((T, k_top), dtype=torch.float32, device=dev) if with_values else None
+    if T == 0:  # nothing to compute
+        return idx, val
     ws, need = _workspace(OP_FUSED_PREFILL, T, P, k_top, dev, workspace)
     _check(lib.indexer_score_topk_fused_prefill(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), _ptr(w),
@@ -307,6 +315,8 @@ def score_topk_fused_decode(q, k_cache, block_table, seq_lens, query_len: int,
     for o in (idx, val):
         if o is not None and (tuple(o.shape) != (RQ, k_top) or not o.is_contiguous()):
             raise ValueError(f"outputs must be contiguous [{RQ}, {k_top}]")
+    if RQ == 0:  # nothing to compute
+        return idx, val
     ws, need = _workspace(OP_FUSED_DECODE, RQ, max_seq_len, k_top, dev, workspace)
     _check(lib.indexer_score_topk_fused_decode(
         _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), bs, k_cache.stride(1),

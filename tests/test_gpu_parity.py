@@ -163,6 +163,56 @@ def test_fused_decode_reuses_workspace():
         check_topk_exact(fi, fv, g_t.cpu().numpy(), inp.k_top, where=inp.name)
 
 
+def test_rows_with_nothing_visible():
+    """Degenerate rows through every entry point: prefill rows hidden by a
+    zero visible prefix or by an all -inf mask row, decode requests of length
+    0 and rows that see no key, and k_top above the row length; scores must
+    be -inf exactly there and the selections all padding."""
+    base = W.random_prefill(21, 6, 300, 64, 128, 40, mask_kind="random", w_kind="signed")
+    vis = np.array([0, 1, 300, 150, 299, 77], np.int32)
+    mask = base.mask.copy()
+    mask[3, :] = np.float16(-np.inf)
+    pre = dataclasses.replace(base, vis_len=vis, mask=mask)
+    _full_check(pre, "prefill with hidden rows")
+    g = gpu_score(pre).cpu().numpy()
+    assert np.all(np.isneginf(g[0])) and np.all(np.isneginf(g[3]))
+    fi, fv = gpu_fused(pre)
+    assert np.all(fi[0] == -1) and np.all(fi[3] == -1) and np.all(np.isneginf(fv[0]))
+
+    dec = W.random_decode(22, 5, 3, 64, 128, 64, 1, 200, 16)
+    sl = dec.seq_lens.copy()
+    sl[[0, 2]] = 0
+    sl[4] = 2          # query 0 of request 4 sees no key, query 2 sees two
+    dec = dataclasses.replace(dec, seq_lens=sl)
+    _full_check(dec, "decode with empty requests")
+    gi, _ = gpu_fused(dec)
+    assert np.all(gi[0:3] == -1) and np.all(gi[6:9] == -1) and np.all(gi[12] == -1)
+
+    wide = dataclasses.replace(W.random_prefill(23, 3, 40, 16, 64, 16), k_top=100)
+    gi, gv = gpu_fused(wide)
+    assert gi.shape == (3, 100) and np.all(gi[:, 40:] == -1) and np.all(np.isneginf(gv[:, 40:]))
+    _full_check(wide, "k_top above the row length")
+
+
+def test_zero_rows_are_a_no_op():
+    """Zero query rows (prefill), zero requests (decode) and zero score rows
+    (top-k) return empty results without launching anything."""
+    d = DEV
+    w = torch.ones(64, device=d)
+    q0 = torch.empty((0, 64, 128), dtype=torch.float16, device=d)
+    k = torch.zeros((128, 128), dtype=torch.float16, device=d)
+    assert li.score_prefill(q0, k, w).shape == (0, 128)
+    idx, val = li.score_topk_fused_prefill(q0, k, w, 8)
+    assert idx.shape == (0, 8)
+    kc = torch.zeros((2, 64, 128), dtype=torch.float16, device=d)
+    bt = torch.zeros((0, 2), dtype=torch.int32, device=d)
+    sl = torch.zeros((0,), dtype=torch.int32, device=d)
+    assert li.score_decode(q0, kc, bt, sl, 1, 128, w).shape == (0, 128)
+    idx, val = li.topk(torch.empty((0, 50), device=d), 8)
+    assert idx.shape == (0, 8)
+    torch.cuda.synchronize()
+
+
 def test_decode_with_mask_and_signed_weights():
     inp = W.random_decode(42, 4, 4, 64, 128, 64, 50, 400, 32, w_kind="signed", mask_kind="bias")
     _full_check(inp, inp.name)
