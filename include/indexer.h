@@ -34,8 +34,12 @@
  *    -inf and NaN are never selected and -0 ties with +0.  Rows with fewer
  *    than k_top selectable keys are padded with index -1 and value -inf.
  *  - Supported shapes (others return INDEXER_ENOTSUP, as a backend's
- *    supports_op check would): n_heads in {4, 8, 16, 32, 64}; head_dim in
- *    {64, 128}; 1 <= k_top <= INDEXER_MAX_K_TOP.
+ *    supports_op check would): 1 <= n_heads <= 64; head_dim in {64, 128};
+ *    1 <= k_top <= INDEXER_MAX_K_TOP.  Kernels are compiled for 4, 8, 16, 32
+ *    and 64 heads; other counts run as the next of those with the last head
+ *    tile zero-filled (the b11372 notes' Metal kernel does the same): the
+ *    extra heads read a real head's q and weigh exactly zero, and no byte past
+ *    q's or w's n_heads heads is read.
  *  - Alignment: q, k (or k_cache) and every q/k row must be 16-byte aligned
  *    (strides multiples of 8 elements); score and w 4-byte aligned.
  *  - Thread safety: every entry point may be called from any host thread;

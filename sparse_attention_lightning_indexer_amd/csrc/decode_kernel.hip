@@ -25,6 +25,8 @@
 //    mapping, and one cross-lane add per key.
 #include <math.h>
 
+#include <atomic>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -101,7 +103,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(ScoreArgs a) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
             const int head = head0 + mb * (SPLIT ? 16 : G::HPB);
-            const _Float16 *src = a.q + (int64_t)t * a.q_st + (int64_t)head * a.q_sh + kh * (D / 2);
+            const _Float16 *src = a.q + (int64_t)t * a.q_st + (int64_t)real_head(head, a.n_heads) * a.q_sh + kh * (D / 2);
 #pragma unroll
             for (int kk = 0; kk < G::KSTEPS; ++kk)
                 qa[mb][kk] = ok ? *reinterpret_cast<const half8 *>(src + kk * 8) : half8{};
@@ -115,7 +117,11 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(ScoreArgs a) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) wv[mb][r] = a.w[kh * (H / 2) + mb * 16 + r];
+            for (int r = 0; r < 16; ++r) {
+                const float w_lo = head_weight((const_f32 *)a.w, mb * 16 + r, a.n_heads);
+                const float w_hi = head_weight((const_f32 *)a.w, H / 2 + mb * 16 + r, a.n_heads);
+                wv[mb][r] = kh ? w_hi : w_lo;
+            }
     }
 
     // rows this lane writes and their visible prefixes (query j of the
@@ -242,7 +248,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(ScoreArgs a) {
                         for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                             for (int rr = 0; rr < 4 * G::G; ++rr)
-                                sum = fmaf(relu(acc[mb][4 * G::G * j + rr]), wc[mb * G::HPB + rr], sum);
+                                sum = fmaf(relu(acc[mb][4 * G::G * j + rr]), head_weight(wc, mb * G::HPB + rr, a.n_heads), sum);
                         if (vis[j]) res[i][j] = sum + (float)mv[i][j];
                     }
                 }
@@ -362,11 +368,11 @@ static_assert(StreamGeo<4, 128, false, 1>::lds_bytes() <= 160 * 1024, "LDS budge
 // row m of M-block mb is head (m>>2 & 1)*H/2 + (m>>3)*4 + (m&3) + 16*mb.
 template <int H, int D, int MB, int KS>
 __device__ __forceinline__ void load_q_split(half8 (&qa)[MB][KS], const _Float16 *qp, int64_t q_st,
-                                             int64_t q_sh, int t, int m, int kh) {
+                                             int64_t q_sh, int t, int m, int kh, int n_heads) {
     const int head0 = ((m >> 2) & 1) * (H / 2) + (m >> 3) * 4 + (m & 3);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        const _Float16 *src = qp + (int64_t)t * q_st + (int64_t)(head0 + mb * 16) * q_sh + kh * (D / 2);
+        const _Float16 *src = qp + (int64_t)t * q_st + (int64_t)real_head(head0 + mb * 16, n_heads) * q_sh + kh * (D / 2);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) qa[mb][kk] = *reinterpret_cast<const half8 *>(src + kk * 8);
     }
@@ -377,14 +383,14 @@ __device__ __forceinline__ void load_q_split(half8 (&qa)[MB][KS], const _Float16
 // never kept.
 template <int H, int D, int MB, int KS>
 __device__ __forceinline__ void load_q_rows(half8 (&qa)[MB][KS], const _Float16 *qp, int64_t q_st,
-                                            int64_t q_sh, int row0, int rhi, int tg, int m, int kh) {
+                                            int64_t q_sh, int row0, int rhi, int tg, int m, int kh, int n_heads) {
     using G = Geo<H, D>;
     const int t = row0 + tg * G::TPB + (((m >> 3) / G::G) << 1) + ((m >> 2) & 1);
     const int tc = t < rhi ? t : row0;
     const int head0 = ((m >> 3) % G::G) * 4 + (m & 3);
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) {
-        const _Float16 *src = qp + (int64_t)tc * q_st + (int64_t)(head0 + mb * G::HPB) * q_sh + kh * (D / 2);
+        const _Float16 *src = qp + (int64_t)tc * q_st + (int64_t)real_head(head0 + mb * G::HPB, n_heads) * q_sh + kh * (D / 2);
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk) qa[mb][kk] = *reinterpret_cast<const half8 *>(src + kk * 8);
     }
@@ -443,6 +449,7 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
     const _Float16 *const maskp = args.mask;        // nullable
     const int64_t mask_st = args.mask_st;
     const float *const wp = args.w;
+    const int nh = args.n_heads;
     float *const scorep = args.score;
     const int64_t score_st = args.score_st;
     const int n_cols = args.n_cols, Q = args.q_per_req, gpr = args.groups_per_req, n_rg = args.n_row_groups;
@@ -605,7 +612,8 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
 #pragma unroll
                     for (int x = 0; x < SG::QL / kPcProducers; ++x) {
                         const int f = x * kPcProducers + p;
-                        dma16(src0 + (int64_t)(head0 + (f / KS) * 16) * q_sh + (f % KS) * 8, slot + f * 1024);
+                        const int hq = nh == H ? head0 + (f / KS) * 16 : real_head(head0 + (f / KS) * 16, nh);
+                        dma16(src0 + (int64_t)hq * q_sh + (f % KS) * 8, slot + f * 1024);
                     }
                     issued += SG::QL / kPcProducers;
                 }
@@ -696,7 +704,15 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
             for (int mb = 0; mb < MB; ++mb)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
-                    wv[mb][r] = kh ? wc[H / 2 + mb * 16 + r] : wc[mb * 16 + r];
+                    float w_lo, w_hi;  // uniform indices: scalar loads, batched when no head is padded
+                    if (nh == H) {
+                        w_lo = wc[mb * 16 + r];
+                        w_hi = wc[H / 2 + mb * 16 + r];
+                    } else {
+                        w_lo = head_weight(wc, mb * 16 + r, nh);
+                        w_hi = head_weight(wc, H / 2 + mb * 16 + r, nh);
+                    }
+                    wv[mb][r] = kh ? w_hi : w_lo;
                     asm volatile("" : "+v"(wv[mb][r]));  // keep in a register, not reloaded per tile
                 }
         }
@@ -729,9 +745,9 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
                 } else {
                     if constexpr (SPLIT) {
                         const int t = row0 + tg < rhi ? row0 + tg : row0;
-                        load_q_split<H, D, MB, KS>(qa, qp, q_st, q_sh, t, m, kh);
+                        load_q_split<H, D, MB, KS>(qa, qp, q_st, q_sh, t, m, kh, nh);
                     } else {
-                        load_q_rows<H, D, MB, KS>(qa, qp, q_st, q_sh, row0, rhi, tg, m, kh);
+                        load_q_rows<H, D, MB, KS>(qa, qp, q_st, q_sh, row0, rhi, tg, m, kh, nh);
                     }
                 }
 #pragma unroll
@@ -826,7 +842,7 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
                         res[j] = 0.0f;
 #pragma unroll
                         for (int rr = 0; rr < 4 * G::G; ++rr)
-                            res[j] = fmaf(relu(cur[4 * G::G * j + rr]), wc[rr], res[j]);
+                            res[j] = fmaf(relu(cur[4 * G::G * j + rr]), head_weight(wc, rr, nh), res[j]);
                     }
                     store_block(res, nb);
                 }
@@ -858,11 +874,11 @@ template <int H, int D, bool SPLIT, int NC>
 hipError_t launch_stream(const ScoreArgs &a, int n_req, hipStream_t stream) {
     auto kern = stream_pc_kernel<H, D, SPLIT, NC>;
     const size_t bytes = StreamGeo<H, D, SPLIT, NC>::lds_bytes();
-    static bool attr = false;
-    if (!attr) {
+    static std::atomic<bool> attr{false};  // per kernel instance
+    if (!attr.load(std::memory_order_relaxed)) {
         hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
         if (e != hipSuccess) return e;
-        attr = true;
+        attr.store(true, std::memory_order_relaxed);
     }
     hipLaunchKernelGGL(kern, dim3(device_cu_count()), dim3((kPcConsumers + kPcProducers) * 64), bytes, stream, a, n_req);
     return hipGetLastError();

@@ -45,6 +45,15 @@ __device__ __forceinline__ int swz(int n) {
 // and branches that depend on it run on the scalar unit.
 __device__ __forceinline__ int uni(int x) { return __builtin_amdgcn_readfirstlane(x); }
 
+// Head counts below the compiled tile run as the next compiled count: the
+// extra heads read a real head's q (any finite values do) and weigh zero, so
+// they add exactly nothing to the score.
+__device__ __forceinline__ int real_head(int head, int n_heads) { return head < n_heads ? head : n_heads - 1; }
+__device__ __forceinline__ float head_weight(const __attribute__((address_space(4))) float *w, int head, int n_heads) {
+    const float v = w[real_head(head, n_heads)];
+    return head < n_heads ? v : 0.0f;
+}
+
 __device__ __forceinline__ bool half_is_neg_inf(_Float16 h) {
     return __builtin_bit_cast(unsigned short, h) == 0xfc00u;
 }

@@ -49,7 +49,7 @@ size_t round_up(size_t v, size_t m) { return (v + m - 1) / m * m; }
 indexer_status check_q_w(const void *q, int64_t q_stride_t, int64_t q_stride_h, const float *w,
                          int32_t n_heads, int32_t head_dim) {
     if (!lidx::score_shape_supported(n_heads, head_dim))
-        return fail(INDEXER_ENOTSUP, "n_heads=%d head_dim=%d not supported (n_heads in {4,8,16,32,64}, head_dim in {64,128})",
+        return fail(INDEXER_ENOTSUP, "n_heads=%d head_dim=%d not supported (n_heads in 1..64, head_dim in {64,128})",
                     n_heads, head_dim);
     if (!q) return fail(INDEXER_EINVAL, "q is NULL");
     if (!w) return fail(INDEXER_EINVAL, "w is NULL");
@@ -196,8 +196,11 @@ lidx::ScoreArgs decode_args(const void *q, int64_t q_stride_t, int64_t q_stride_
     return a;
 }
 
-indexer_status run_score(lidx::ScoreArgs &a, int n_heads, int head_dim, bool paged, int n_requests,
+indexer_status run_score(lidx::ScoreArgs &a, int n_heads_real, int head_dim, bool paged, int n_requests,
                          hipStream_t stream) {
+    // the kernels run the next compiled head count; the extra heads weigh 0
+    a.n_heads = n_heads_real;
+    const int n_heads = lidx::compiled_heads(n_heads_real);
     lidx::ScorePlan p = paged ? lidx::plan_decode(a, n_heads, head_dim, n_requests)
                               : lidx::plan_score(a, n_heads, head_dim);
     if ((int64_t)a.n_row_groups * a.n_chunks > INT32_MAX)

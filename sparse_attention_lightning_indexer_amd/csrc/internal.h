@@ -23,6 +23,7 @@ struct ScoreArgs {
     int32_t bs_shift;           // log2(block_size) if a power of two, else -1
     const int32_t *seq_lens;    // paged only
     const float *w;
+    int32_t n_heads;            // heads of q and w; the kernel's tile may be larger (extra heads weigh 0)
     const _Float16 *mask;
     int64_t mask_st;
     const int32_t *vis_len;     // contiguous only (nullable)
@@ -51,6 +52,8 @@ struct ScorePlan {
 };
 
 bool score_shape_supported(int n_heads, int head_dim);
+// The smallest compiled head count (4, 8, 16, 32, 64) holding n_heads.
+int compiled_heads(int n_heads);
 // Contiguous keys (score_kernel.hip).  Fills the launch-geometry fields of
 // `a` and returns the plan.
 ScorePlan plan_score(ScoreArgs &a, int n_heads, int head_dim);

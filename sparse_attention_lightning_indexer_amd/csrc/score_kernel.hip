@@ -36,6 +36,8 @@
 // has its own latency-oriented kernel (decode_kernel.hip).
 #include <math.h>
 
+#include <atomic>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -45,7 +47,9 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 
-template <int H, int D, int NBW>
+// PAD: fewer real heads than H (the extra heads weigh 0).  Kept a separate
+// instance so that the full-head kernel's weights stay plain scalar loads.
+template <int H, int D, int NBW, bool PAD>
 __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
     using G = Geo<H, D>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -152,7 +156,8 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
 #pragma unroll
         for (int mb = 0; mb < G::MBLK; ++mb) {
             const _Float16 *src = a.q + (int64_t)t * a.q_st +
-                                  (int64_t)(mb * G::HPB + head_m) * a.q_sh + kh * (D / 2);
+                                  (int64_t)(PAD ? real_head(mb * G::HPB + head_m, a.n_heads) : mb * G::HPB + head_m) * a.q_sh +
+                                  kh * (D / 2);
 #pragma unroll
             for (int kk = 0; kk < G::KSTEPS; ++kk) {
                 if (ok) {
@@ -289,7 +294,7 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
 #pragma unroll
                         for (int rr = 0; rr < 4 * G::G; ++rr)
                             sum = fmaf(relu(acc[mb][4 * G::G * j + rr]),
-                                       wc[mb * G::HPB + rr], sum);
+                                       PAD ? head_weight(wc, mb * G::HPB + rr, a.n_heads) : wc[mb * G::HPB + rr], sum);
                     if (vis[j]) res[j] = sum + (float)mcur[nb][j];
                 }
             }
@@ -329,30 +334,29 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
 
 // Dynamic LDS above 64 KiB must be enabled per kernel; done once per
 // instantiation for the largest size used so far.
-template <typename K>
-hipError_t allow_lds(K kern, size_t bytes) {
-    static int allowed = 65536;
-    if ((int)bytes <= allowed) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute((const void *)kern,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e == hipSuccess) allowed = (int)bytes;
+template <auto Kern>
+hipError_t allow_lds(size_t bytes) {
+    static std::atomic<int> allowed{65536};  // per kernel instance: the attribute is per kernel
+    if ((int)bytes <= allowed.load(std::memory_order_relaxed)) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute((const void *)Kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) allowed.store((int)bytes, std::memory_order_relaxed);
     return e;
+}
+
+template <int H, int D, int NBW, bool PAD>
+hipError_t launch_one(const ScoreArgs &a, const ScorePlan &p, hipStream_t stream) {
+    auto kern = score_kernel<H, D, NBW, PAD>;
+    hipError_t e = allow_lds<score_kernel<H, D, NBW, PAD>>(p.lds_bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, p.grid, dim3(kThreads), p.lds_bytes, stream, a);
+    return hipGetLastError();
 }
 
 template <int H, int D>
 hipError_t launch_hd(const ScoreArgs &a, const ScorePlan &p, hipStream_t stream) {
-    if (p.nbw == 4) {
-        auto kern = score_kernel<H, D, 4>;
-        hipError_t e = allow_lds(kern, p.lds_bytes);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, p.grid, dim3(kThreads), p.lds_bytes, stream, a);
-    } else {
-        auto kern = score_kernel<H, D, 1>;
-        hipError_t e = allow_lds(kern, p.lds_bytes);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(kern, p.grid, dim3(kThreads), p.lds_bytes, stream, a);
-    }
-    return hipGetLastError();
+    if (a.n_heads == H)
+        return p.nbw == 4 ? launch_one<H, D, 4, false>(a, p, stream) : launch_one<H, D, 1, false>(a, p, stream);
+    return p.nbw == 4 ? launch_one<H, D, 4, true>(a, p, stream) : launch_one<H, D, 1, true>(a, p, stream);
 }
 
 template <int H>
@@ -363,9 +367,13 @@ hipError_t launch_h(const ScoreArgs &a, const ScorePlan &p, int D, hipStream_t s
 }  // namespace
 
 bool score_shape_supported(int n_heads, int head_dim) {
-    const bool h_ok = n_heads == 4 || n_heads == 8 || n_heads == 16 || n_heads == 32 || n_heads == 64;
-    const bool d_ok = head_dim == 64 || head_dim == 128;
-    return h_ok && d_ok;
+    return n_heads >= 1 && n_heads <= 64 && (head_dim == 64 || head_dim == 128);
+}
+
+int compiled_heads(int n_heads) {
+    int h = 4;
+    while (h < n_heads) h *= 2;
+    return h;
 }
 
 ScorePlan plan_score(ScoreArgs &a, int n_heads, int head_dim) {

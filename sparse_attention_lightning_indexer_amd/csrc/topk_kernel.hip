@@ -17,6 +17,8 @@
 //    the bin of the k-th key and gather the candidates into LDS, which are
 //    then selected and ordered the same way.
 //  * topk_row_general: the fully general streaming fallback (heavy ties).
+#include <atomic>
+
 #include "internal.h"
 
 #include <math.h>
@@ -534,12 +536,12 @@ __global__ void __launch_bounds__(kThreads, 1) topk_long_kernel(TopkArgs a, int 
 //    bigger than kMaxBucket (heavy ties) use a plain bitonic sort instead.
 // ---------------------------------------------------------------------------
 
-template <typename K>
-hipError_t allow_lds(K kern, size_t bytes) {
-    static int allowed = 65536;
-    if ((int)bytes <= allowed) return hipSuccess;
-    hipError_t e = hipFuncSetAttribute((const void *)kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
-    if (e == hipSuccess) allowed = (int)bytes;
+template <auto Kern>
+hipError_t allow_lds(size_t bytes) {
+    static std::atomic<int> allowed{65536};  // per kernel instance: the attribute is per kernel
+    if ((int)bytes <= allowed.load(std::memory_order_relaxed)) return hipSuccess;
+    hipError_t e = hipFuncSetAttribute((const void *)Kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) allowed.store((int)bytes, std::memory_order_relaxed);
     return e;
 }
 
@@ -1001,7 +1003,7 @@ template <int THREADS, int E>
 hipError_t launch_rows(const TopkArgs &a, int k_pad, hipStream_t stream) {
     auto kern = topk_rows_kernel<THREADS, E>;
     const size_t bytes = rows_lds_bytes<THREADS, E>(k_pad);
-    hipError_t e = allow_lds(kern, bytes);
+    hipError_t e = allow_lds<topk_rows_kernel<THREADS, E>>(bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(a.n_rows), dim3(THREADS), bytes, stream, a, k_pad);
     return hipGetLastError();
@@ -1035,7 +1037,7 @@ hipError_t launch_topk(const TopkArgs &a, void *, hipStream_t stream) {
         return launch_rows<1024, 16>(a, k_pad, stream);
     }
     const size_t bytes = long_lds_bytes(k_pad);
-    hipError_t e = allow_lds(topk_long_kernel, bytes);
+    hipError_t e = allow_lds<topk_long_kernel>(bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(topk_long_kernel, dim3(a.n_rows), dim3(kThreads), bytes, stream, a, k_pad);
     return hipGetLastError();

@@ -63,7 +63,8 @@ def prefill(lib, **kw):
 
 
 @pytest.mark.parametrize("kw,status,msg", [
-    (dict(H=12), li.ENOTSUP, b"n_heads=12"),
+    (dict(H=0), li.ENOTSUP, b"n_heads=0"),
+    (dict(H=65), li.ENOTSUP, b"n_heads=65"),
     (dict(H=128), li.ENOTSUP, b"not supported"),
     (dict(d=96, qsh=96, qst=96 * 64, kss=96), li.ENOTSUP, b"head_dim=96"),
     (dict(q=None), li.EINVAL, b"q is NULL"),
@@ -106,7 +107,7 @@ def decode(lib, **kw):
     (dict(bt=None), li.EINVAL, b"block_table is NULL"),
     (dict(sl=None), li.EINVAL, b"seq_lens is NULL"),
     (dict(kc=None), li.EINVAL, b"k_cache is NULL"),
-    (dict(H=6), li.ENOTSUP, b"n_heads=6"),
+    (dict(H=96), li.ENOTSUP, b"n_heads=96"),
     (dict(sst=100), li.EINVAL, b"score_stride_t"),
     (dict(R=70000, Q=70000), li.EINVAL, b"int32"),
 ])

@@ -163,6 +163,35 @@ def test_fused_decode_reuses_workspace():
         check_topk_exact(fi, fv, g_t.cpu().numpy(), inp.k_top, where=inp.name)
 
 
+# head counts the kernels are not compiled for: the last head tile is
+# zero-filled (extra heads weigh 0); every path, with the oracle on the real heads
+ODD_HEAD_CASES = [
+    # kind, H, d, (prefill T, P) or (decode R, Q, lo, hi)
+    ("prefill", 1, 64, (9, 130)),
+    ("prefill", 3, 128, (21, 333)),
+    ("prefill", 12, 64, (17, 257)),
+    ("prefill", 24, 128, (33, 400)),
+    ("prefill", 48, 128, (40, 700)),
+    ("prefill", 63, 64, (11, 300)),
+    ("decode", 5, 128, (40, 1, 1, 700)),
+    ("decode", 20, 64, (30, 3, 1, 900)),
+    ("decode", 40, 128, (50, 1, 1, 1500)),
+    ("decode", 56, 128, (20, 4, 4, 1000)),
+]
+
+
+@pytest.mark.parametrize("kind,H,d,shape", ODD_HEAD_CASES,
+                         ids=[f"{c[0]}-H{c[1]}-d{c[2]}" for c in ODD_HEAD_CASES])
+def test_any_head_count(kind, H, d, shape):
+    if kind == "prefill":
+        T, P = shape
+        inp = W.random_prefill(300 + H, T, P, H, d, 24, mask_kind="random", w_kind="signed")
+    else:
+        R, Q, lo, hi = shape
+        inp = W.random_decode(400 + H, R, Q, H, d, 64, lo, hi, 24, w_kind="signed")
+    _full_check(inp, f"{kind} H={H} d={d}")
+
+
 def test_rows_with_nothing_visible():
     """Degenerate rows through every entry point: prefill rows hidden by a
     zero visible prefix or by an all -inf mask row, decode requests of length
