@@ -380,7 +380,7 @@ def main():
             roof["measured_peak"] = measured
             roof["frac_of_measured"] = roof["achieved"] / measured
             roof["measured_peak_probe"] = ("streaming read of 4 GiB" if roof["bound"] == "hbm" else
-                                           "f16 MFMA 32x32x16, B fragments from LDS, 2 waves per SIMD")
+                                           "f16 MFMA 32x32x16, B fragments from LDS, 2 waves per SIMD, random operands")
 
     line = {
         "metric": "indexer score+top-k: (token,key) pairs/s; % of MFMA or HBM roofline",

@@ -225,7 +225,8 @@ size_t indexer_workspace_bytes(int op, int32_t n_rows, int32_t n_cols, int32_t k
  * indexer_probe_mfma -- 2 workgroups of 256 threads per compute unit, each
  *   wave running iters x 128 v_mfma_f32_32x32x16_f16 fed as the score
  *   kernels feed them (B fragments from swizzled LDS rows, four accumulators
- *   per fragment, two fragments in flight).  *flops receives the f16 flops of
+ *   per fragment, two fragments in flight), on pseudo-random f16 operands
+ *   (the rate depends on the operand bits).  *flops receives the f16 flops of
  *   the launch.  sink: device buffer of indexer_probe_sink_floats() floats
  *   (written only in a case that never occurs).  EINVAL for iters < 1 or a
  *   NULL pointer.

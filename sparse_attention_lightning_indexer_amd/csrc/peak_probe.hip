@@ -6,7 +6,10 @@
 //    kernels feed it -- A fragments in registers, one 16-byte B fragment per
 //    lane read from XOR-swizzled LDS rows per K step, shared by four M-blocks
 //    (four independent accumulators), the next two fragments in flight.  Two
-//    workgroups of four waves per compute unit (two waves per SIMD).
+//    workgroups of four waves per compute unit (two waves per SIMD).  The
+//    operands are pseudo-random f16 values (every mantissa bit in play):
+//    the sustained rate depends on the data, and near-constant operands run
+//    about a quarter faster than the N(0,1)-like q and keys of real inputs.
 //  * probe_read_kernel: a large streaming read, 16 bytes per lane per load,
 //    eight workgroups of 256 threads per compute unit.
 // Both keep their results live through a store that never happens.
@@ -20,10 +23,22 @@ constexpr int kProbeMB = 4;      // accumulators fed by one B fragment
 constexpr int kProbeBlocks = 4;  // 32-key blocks per LDS tile
 constexpr int kProbePF = 2;      // B fragments in flight
 
-__global__ void __launch_bounds__(256) probe_mfma_kernel(int iters, float *sink) {
+// A pseudo-random f16 in [-2, 2) from a 32-bit counter (an integer hash
+// whose output bits all depend on every input bit).
+__device__ __forceinline__ _Float16 probe_value(uint32_t x) {
+    x *= 0x9e3779b1u;
+    x ^= x >> 15;
+    x *= 0x85ebca77u;
+    x ^= x >> 13;
+    return (_Float16)((float)(x >> 8) * (4.0f / 16777216.0f) - 2.0f);
+}
+
+__global__ void __launch_bounds__(256, 2) probe_mfma_kernel(int iters, float *sink) {
     __shared__ __attribute__((aligned(16))) unsigned char tile[kProbeBlocks * 32 * 256];
     const int lane = threadIdx.x & 63, m = lane & 31, kh = lane >> 5;
-    for (int i = threadIdx.x; i < (int)sizeof(tile) / 4; i += 256) ((float *)tile)[i] = 1e-3f * (float)(i & 7);
+    const uint32_t seed = (uint32_t)blockIdx.x * 0x10000u;
+    for (int i = threadIdx.x; i < (int)sizeof(tile) / 2; i += 256)
+        ((_Float16 *)tile)[i] = probe_value(seed + (uint32_t)i);
     __syncthreads();
     half8 a[kProbeMB][8];
 #pragma unroll
@@ -31,16 +46,23 @@ __global__ void __launch_bounds__(256) probe_mfma_kernel(int iters, float *sink)
 #pragma unroll
         for (int kk = 0; kk < 8; ++kk)
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a[mb][kk][e] = (_Float16)(1e-2f * (float)(mb + kk + e + lane));
+            for (int e = 0; e < 8; ++e)
+                a[mb][kk][e] = probe_value(seed + 0x8000u + (uint32_t)(((mb * 8 + kk) * 64 + lane) * 8 + e));
     f32x16 acc[kProbeMB];
 #pragma unroll
     for (int mb = 0; mb < kProbeMB; ++mb) acc[mb] = f32x16{};
-    const lds_half8 *rows = (const lds_half8 *)tile;
+    // byte offset of this lane's fragment for K step kk inside a 32-key block
+    // (the row stays m, so the swizzle term is the same for every block)
+    int off[8];
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) off[kk] = m * 256 + (((kh * 8 + kk) ^ (m & 15)) << 4);
     auto frag = [&](int blk, int kk) {
-        const int n = blk * 32 + m;
-        return rows[n * 16 + ((kh * 8 + kk) ^ (n & 15))];
+        return *(const lds_half8 *)(tile + blk * 8192 + off[kk]);
     };
     for (int it = 0; it < iters; ++it) {
+        // the tile is not written in the loop: without this the compiler
+        // would hoist every fragment read out of it into registers
+        asm volatile("" ::: "memory");
 #pragma unroll
         for (int blk = 0; blk < kProbeBlocks; ++blk) {
             half8 bq[kProbePF];
