@@ -330,7 +330,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(ScoreArgs a) {
 
 constexpr int kPcProducers = 4;                        // load waves, one per SIMD
 constexpr int kStreamTK = 128;                         // keys per tile
-constexpr int kStreamNBUF = 3;                         // tiles in the LDS rings
+constexpr int kStreamNBUF = 3;                         // tiles in the LDS rings (4 where they fit, below)
 constexpr int kMaxRG = 1536;                           // row groups handled in-kernel
 constexpr int kBtLead = 3;                             // block ids fetched this many tiles ahead
 constexpr int kBtRing = kBtLead + 3;                   // block-id ring slots
@@ -355,10 +355,19 @@ struct StreamGeo {
     static constexpr int MSLOT = MROWS4 * 1024;                // bytes of one mask slot
     static constexpr int DPT = kStreamTK * G::CPR / 64 / kPcProducers;  // key loads per producer per tile
     static constexpr int NBW = kStreamTK / (32 * NC);          // 32-key blocks per consumer per tile
-    static constexpr size_t lds_bytes() {
-        return (size_t)kStreamNBUF * (TILE_BYTES + MSLOT) + 2 * (size_t)QSLOT + 4 * (3 * (size_t)kMaxRG + 1) +
+    static constexpr size_t lds_bytes_for(int nbuf) {
+        return (size_t)nbuf * (TILE_BYTES + MSLOT) + 2 * (size_t)QSLOT + 4 * (3 * (size_t)kMaxRG + 1) +
                4 * (size_t)kPcProducers * kBtRing * 64 + 128;
     }
+    // Ring depth and publication lag.  A producer publishes tile j once it
+    // has issued tile j + LAG, so LAG + 1 tiles are in flight while the
+    // consumers work on an older one; that needs NBUF >= LAG + 2.  With q
+    // through the LDS slots a new row group's slot waits for the consumers
+    // to pass the first tile of the group two back, which may be the tile
+    // just before: only LAG 1 lets them get there, so those keep 3 and 1.
+    static constexpr int NBUF = (!QLDS && lds_bytes_for(4) <= 160 * 1024) ? 4 : kStreamNBUF;
+    static constexpr int LAG = NBUF - 2;
+    static constexpr size_t lds_bytes() { return lds_bytes_for(NBUF); }
 };
 
 static_assert(StreamGeo<64, 128, true, 4>::lds_bytes() <= 160 * 1024, "LDS budget");
@@ -457,8 +466,8 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
     extern __shared__ __attribute__((aligned(16))) unsigned char smem_raw[];
     lds_u8 *const smem = (lds_u8 *)smem_raw;
     lds_u8 *const keys = smem;
-    lds_u8 *const mslots = smem + kStreamNBUF * TILE_BYTES;                        // [NBUF][MSLOT]
-    lds_u8 *const qslots = mslots + kStreamNBUF * SG::MSLOT;                       // QLDS: 2 slots
+    lds_u8 *const mslots = smem + SG::NBUF * TILE_BYTES;                           // [NBUF][MSLOT]
+    lds_u8 *const qslots = mslots + SG::NBUF * SG::MSLOT;                          // QLDS: 2 slots
     lds_i32 *const pref = (lds_i32 *)(qslots + 2 * SG::QSLOT);                     // [n_rg + 1]
     lds_i32 *const gbd = pref + kMaxRG + 1;                                        // [n_rg] keys visible to the group
     lds_i32 *const slen = gbd + kMaxRG;                                            // [n_req]
@@ -523,20 +532,27 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
     const int rg_first = n_mine > 0 ? uni(misc[8]) : 0;
 
     // per-tile cursor (wave-uniform): row group, its ordinal among this
-    // workgroup's row groups, first key, keys visible to the group
-    // (advance: the cursor of tile j from that of tile j-1)
-#define LIDX_ADVANCE(rg, ord, s0, bound, j)                 \
+    // workgroup's row groups, first key, keys visible to the group, and the
+    // group's tile range [lo, hi) in registers, so that a step inside the
+    // group reads no LDS (advance: the cursor of tile j from that of j-1)
+#define LIDX_ADVANCE(rg, ord, s0, bound, lo, hi, j)          \
     do {                                                     \
         const int t_ = t_begin + (j);                        \
-        int e_ = rg;                                         \
-        while (uni(pref[e_ + 1]) <= t_) ++e_;                \
-        ord += e_ != rg ? 1 : 0;                             \
-        rg = e_;                                             \
-        s0 = (t_ - uni(pref[e_])) * TK;                      \
-        bound = uni(gbd[e_]);                                \
+        if (t_ >= hi) {                                      \
+            int e_ = rg + 1;                                 \
+            while (uni(pref[e_ + 1]) <= t_) ++e_;            \
+            ++ord;                                           \
+            rg = e_;                                         \
+            lo = uni(pref[e_]);                              \
+            hi = uni(pref[e_ + 1]);                          \
+            bound = uni(gbd[e_]);                            \
+        }                                                    \
+        s0 = (t_ - lo) * TK;                                 \
     } while (0)
 
-    const int s0_first = (t_begin - (n_mine > 0 ? uni(pref[rg_first]) : 0)) * TK;
+    const int lo_first = n_mine > 0 ? uni(pref[rg_first]) : 0;
+    const int hi_first = n_mine > 0 ? uni(pref[rg_first + 1]) : 0;
+    const int s0_first = (t_begin - lo_first) * TK;
     const int bd_first = n_mine > 0 ? uni(gbd[rg_first]) : 0;
 
     if (wid >= NCONS) {
@@ -545,10 +561,13 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
         const int p = wid - NCONS;
         lds_i32 *const bt_mine = btr + p * kBtRing * 64;
         int k_rg = rg_first, k_ord = 0, k_s0 = s0_first, k_bd = bd_first;     // tile j
+        int k_lo = lo_first, k_hi = hi_first;
         int b_rg = rg_first, b_ord = 0, b_s0 = s0_first, b_bd = bd_first;     // tile next_bt
+        int b_lo = lo_first, b_hi = hi_first;
         int next_bt = 0, issued = 0;
         int mbt0 = 0, mbt1 = 0, mbt2 = 0, mbt3 = 0;  // `issued` after the block ids of tiles j..j+3
-        int last_ord = -1, gf1 = -1, gf2 = -1, mk_prev = 0;
+        int last_ord = -1, gf1 = -1, gf2 = -1;
+        int mk1 = 0, mk2 = 0;  // `issued` after the loads of tiles j-1 and j-2
 
         // One 16-byte-per-lane load covers KPI consecutive keys (lane l: key
         // l / CPR, chunk l % CPR).  When the block size is a multiple of KPI
@@ -577,18 +596,18 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
             else if (o_ == 2) mbt2 = issued;                                                       \
             else mbt3 = issued;                                                                    \
             ++next_bt;                                                                             \
-            if (next_bt < n_mine) LIDX_ADVANCE(b_rg, b_ord, b_s0, b_bd, next_bt);                  \
+            if (next_bt < n_mine) LIDX_ADVANCE(b_rg, b_ord, b_s0, b_bd, b_lo, b_hi, next_bt);      \
         }
 
         for (int j = 0; j < n_mine; ++j) {
-            if (j > 0) LIDX_ADVANCE(k_rg, k_ord, k_s0, k_bd, j);
+            if (j > 0) LIDX_ADVANCE(k_rg, k_ord, k_s0, k_bd, k_lo, k_hi, j);
             LIDX_ISSUE_BT(j + kBtLead);
             wait_vmem_below(issued - mbt0);  // block ids of tile j are in LDS
 
             // the ring slot of tile j last held tile j - NBUF; a new row
             // group's q slot last held the group two back
             const bool newg = k_ord != last_ord;
-            int need = j - kStreamNBUF + 1;
+            int need = j - SG::NBUF + 1;
             if (QLDS && newg && gf2 >= 0) need = max(need, gf2 + 1);
             if (need > 0) {
                 for (;;) {
@@ -626,7 +645,7 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
             // visible key (their scores are discarded), so every address is a
             // key that exists
             {
-                lds_u8 *base = keys + (j % kStreamNBUF) * TILE_BYTES;
+                lds_u8 *base = keys + (j % SG::NBUF) * TILE_BYTES;
                 if (kpi_blocks) {
                     const lds_i32 *bt = bt_mine + (j % kBtRing) * 64;
                     const int b0 = sh >= 0 ? k_s0 >> sh : k_s0 / bs;
@@ -666,7 +685,7 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
             // rows past the group repeat its first row, chunks past the last
             // column repeat the last full chunk (neither is ever used)
             if (maskp) {
-                lds_u8 *mslot = mslots + (j % kStreamNBUF) * SG::MSLOT;
+                lds_u8 *mslot = mslots + (j % SG::NBUF) * SG::MSLOT;
                 for (int x = p; x < SG::MROWS4; x += kPcProducers) {
                     const int r = x * 4 + (lane >> 4);
                     const int t = row0_k + r < rhi_k ? row0_k + r : row0_k;
@@ -678,12 +697,20 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
             mbt0 = mbt1;
             mbt1 = mbt2;
             mbt2 = mbt3;
-            // tile j-1 (issued one step earlier) is published once it has landed
-            if (j > 0) {
-                wait_vmem_below(issued - mk_prev);
-                if (lane == 0) set_lds_flag(misc + kFlagReady + p, j);
+            // tile j-LAG is published once it has landed
+            if constexpr (SG::LAG == 1) {
+                if (j > 0) {
+                    wait_vmem_below(issued - mk1);
+                    if (lane == 0) set_lds_flag(misc + kFlagReady + p, j);
+                }
+            } else {
+                if (j > 1) {
+                    wait_vmem_below(issued - mk2);
+                    if (lane == 0) set_lds_flag(misc + kFlagReady + p, j - 1);
+                }
             }
-            mk_prev = issued;
+            mk2 = mk1;
+            mk1 = issued;
         }
         if (n_mine > 0) {
             wait_vmem_all();
@@ -695,6 +722,7 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
         // ================= consumers =================
         const int tg = wid / NC, col = wid - tg * NC;
         int c_rg = rg_first, c_ord = 0, c_s0 = s0_first, c_bd = bd_first, q_ord = -1;
+        int c_lo = lo_first, c_hi = hi_first;
         half8 qa[MB][KS];
         int rvis[SLOTS];  // keys visible to this consumer's rows
         const_f32 *wc = (const_f32 *)wp;
@@ -716,9 +744,37 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
                     asm volatile("" : "+v"(wv[mb][r]));  // keep in a register, not reloaded per tile
                 }
         }
+        // q from memory (without the LDS slots) and the visible lengths of
+        // this consumer's rows, for the row group of rows row0 .. rhi-1
+        auto load_q_mem = [&](int row0, int rhi) {
+            if constexpr (SPLIT) {
+                const int t = row0 + tg < rhi ? row0 + tg : row0;
+                load_q_split<H, D, MB, KS>(qa, qp, q_st, q_sh, t, m, kh, nh);
+            } else {
+                load_q_rows<H, D, MB, KS>(qa, qp, q_st, q_sh, row0, rhi, tg, m, kh, nh);
+            }
+        };
+        auto row_lengths = [&](int req_c, int row0, int rhi) {
+#pragma unroll
+            for (int j = 0; j < SLOTS; ++j) {
+                const int tr = SPLIT ? row0 + tg : row0 + tg * TPB + 2 * j + kh;
+                rvis[j] = tr < rhi ? row_vis(req_c, tr) : 0;
+            }
+        };
+        if constexpr (!QLDS) {
+            // the first row group's q loads now, while its first tile is on its way
+            if (n_mine > 0) {
+                const int req_c = c_rg / gpr, sub_c = c_rg - req_c * gpr;
+                const int row0 = req_c * Q + sub_c * ROWS;
+                const int rhi = min(req_c * Q + Q, row0 + ROWS);
+                load_q_mem(row0, rhi);
+                row_lengths(req_c, row0, rhi);
+                q_ord = c_ord;
+            }
+        }
         wait_vmem_all_known();
         for (int i = 0; i < n_mine; ++i) {
-            if (i > 0) LIDX_ADVANCE(c_rg, c_ord, c_s0, c_bd, i);
+            if (i > 0) LIDX_ADVANCE(c_rg, c_ord, c_s0, c_bd, c_lo, c_hi, i);
             for (;;) {  // every producer's part of tile i has landed
                 int mr = lds_flag(misc + kFlagReady);
 #pragma unroll
@@ -743,28 +799,16 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
                         for (int kk = 0; kk < KS; ++kk)
                             qa[mb][kk] = *reinterpret_cast<const lds_half8 *>(slot + (mb * KS + kk) * 1024);
                 } else {
-                    if constexpr (SPLIT) {
-                        const int t = row0 + tg < rhi ? row0 + tg : row0;
-                        load_q_split<H, D, MB, KS>(qa, qp, q_st, q_sh, t, m, kh, nh);
-                    } else {
-                        load_q_rows<H, D, MB, KS>(qa, qp, q_st, q_sh, row0, rhi, tg, m, kh, nh);
-                    }
+                    load_q_mem(row0, rhi);
                 }
-#pragma unroll
-                for (int j = 0; j < SLOTS; ++j) {
-                    int v = 0;
-                    if (trow[j] < rhi) {
-                        v = row_vis(req_c, trow[j]);
-                    }
-                    rvis[j] = v;
-                }
+                row_lengths(req_c, row0, rhi);
                 // a wait the compiler sees: otherwise it cannot tell on later
                 // tiles that q has landed and waits for the score stores too
                 wait_vmem_all_known();
                 q_ord = c_ord;
             }
-            const lds_u8 *tbase = keys + (i % kStreamNBUF) * TILE_BYTES;
-            const lds_u16 *mbase = (const lds_u16 *)(mslots + (i % kStreamNBUF) * SG::MSLOT);
+            const lds_u8 *tbase = keys + (i % SG::NBUF) * TILE_BYTES;
+            const lds_u16 *mbase = (const lds_u16 *)(mslots + (i % SG::NBUF) * SG::MSLOT);
 
             // visibility, mask, store of the row sums of 32-key block nb
             auto store_block = [&](const float (&res)[SLOTS], int nb) {
