@@ -267,10 +267,8 @@ def main():
     score = torch.empty((n_rows, n_cols), dtype=torch.float32, device=dev)
     idx = torch.empty((n_rows, k_top), dtype=torch.int32, device=dev)
     val = torch.empty((n_rows, k_top), dtype=torch.float32, device=dev)
-    ws = None
-    if paged:
-        ws = torch.empty(li.workspace_bytes(li.OP_FUSED_DECODE, n_rows, n_cols, k_top), dtype=torch.uint8,
-                         device=dev)
+    op = li.OP_FUSED_DECODE if paged else li.OP_FUSED_PREFILL
+    ws = torch.empty(li.workspace_bytes(op, n_rows, n_cols, k_top), dtype=torch.uint8, device=dev)
 
     def run_score(c):
         if paged:
@@ -280,22 +278,22 @@ def main():
             li.score_prefill(c["q"], c["k"], shared["w"], c["mask"], shared["vis"], out=score)
 
     def run_topk():
-        li.topk(score, k_top, idx=idx, val=val)
+        # as in the fused entry points: a contiguous row's visible prefix
+        # is its row length
+        li.topk(score, k_top, row_len=None if paged else shared["vis"], idx=idx, val=val)
 
     def run_fused(c):
-        li.score_topk_fused_decode(c["q"], c["k"], shared["bt"], shared["sl"], inp.Q, inp.max_seq_len,
-                                   shared["w"], k_top, c["mask"], workspace=ws, idx=idx, val=val)
-
-    # one step: paged keys through the fused entry point (score kernel into
-    # a workspace, then the top-k kernel), contiguous keys as score then
-    # top-k (what the fused prefill entry point does, with the score rows in
-    # a caller-visible buffer)
-    def step(i):
         if paged:
-            run_fused(copies[i % n_copies])
+            li.score_topk_fused_decode(c["q"], c["k"], shared["bt"], shared["sl"], inp.Q, inp.max_seq_len,
+                                       shared["w"], k_top, c["mask"], workspace=ws, idx=idx, val=val)
         else:
-            run_score(copies[i % n_copies])
-            run_topk()
+            li.score_topk_fused_prefill(c["q"], c["k"], shared["w"], k_top, c["mask"], shared["vis"],
+                                        workspace=ws, idx=idx, val=val)
+
+    # one step: the fused entry point (score kernel into a workspace, then
+    # the top-k kernel)
+    def step(i):
+        run_fused(copies[i % n_copies])
 
     if args.calib_copy_mib > 0:
         n = args.calib_copy_mib << 18  # f32 elements

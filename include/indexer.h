@@ -174,9 +174,11 @@ indexer_status indexer_topk(
 /*
  * indexer_score_topk_fused_prefill -- indexer_score_prefill followed by
  * indexer_topk, with the score rows kept in the caller's workspace instead of
- * a caller-visible buffer.  Arguments as in the two calls; workspace must
- * hold indexer_workspace_bytes(INDEXER_OP_FUSED_PREFILL, n_tokens, n_pool,
- * k_top) bytes, 256-byte aligned.
+ * a caller-visible buffer.  Arguments as in the two calls; vis_len (when
+ * given) also serves as the top-k's row_len, since keys at or past
+ * vis_len[t] score -inf by definition (the result is the same).  workspace
+ * must hold indexer_workspace_bytes(INDEXER_OP_FUSED_PREFILL, n_tokens,
+ * n_pool, k_top) bytes, 256-byte aligned.
  */
 indexer_status indexer_score_topk_fused_prefill(
     const void *q, int64_t q_stride_t, int64_t q_stride_h,

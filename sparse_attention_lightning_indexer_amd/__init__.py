@@ -257,8 +257,9 @@ def _workspace(op, n_rows, n_cols, k_top, dev, workspace):
 
 
 def score_topk_fused_prefill(q, k, w, k_top: int, mask=None, vis_len=None,
-                             with_values: bool = True, workspace=None):
-    """indexer_score_prefill + indexer_topk with scores kept in a workspace."""
+                             with_values: bool = True, workspace=None, idx=None, val=None):
+    """indexer_score_prefill + indexer_topk with scores kept in a workspace.
+    `idx` / `val` may be given as outputs ([n_tokens, k_top], contiguous)."""
     torch = _torch()
     lib = load_library()
     dev = _q_checks(q, w)
@@ -274,8 +275,16 @@ def score_topk_fused_prefill(q, k, w, k_top: int, mask=None, vis_len=None,
     if vis_len is not None:
         _need(vis_len, "vis_len", torch.int32, dev, 1)
         vis_len = vis_len.contiguous()
-    idx = torch.empty((T, k_top), dtype=torch.int32, device=dev)
-    val = torch.empty((T, k_top), dtype=torch.float32, device=dev) if with_values else None
+    if idx is None:
+        idx = torch.empty((T, k_top), dtype=torch.int32, device=dev)
+    _need(idx, "idx", torch.int32, dev, 2)
+    if val is None and with_values:
+        val = torch.empty((T, k_top), dtype=torch.float32, device=dev)
+    if val is not None:
+        _need(val, "val", torch.float32, dev, 2)
+    for o in (idx, val):
+        if o is not None and (tuple(o.shape) != (T, k_top) or not o.is_contiguous()):
+            raise ValueError(f"outputs must be contiguous [{T}, {k_top}]")
     if T == 0:  # nothing to compute
         return idx, val
     ws, need = _workspace(OP_FUSED_PREFILL, T, P, k_top, dev, workspace)
@@ -290,9 +299,8 @@ def score_topk_fused_prefill(q, k, w, k_top: int, mask=None, vis_len=None,
 def score_topk_fused_decode(q, k_cache, block_table, seq_lens, query_len: int,
                             max_seq_len: int, w, k_top: int, mask=None,
                             with_values: bool = True, workspace=None, idx=None, val=None):
-    """indexer_score_decode + indexer_topk with scores kept in a workspace
-    (one launch when the selection runs inside the score kernel).  `idx` /
-    `val` may be given as [rows, k_top] outputs."""
+    """indexer_score_decode + indexer_topk with scores kept in a workspace.
+    `idx` / `val` may be given as [rows, k_top] outputs."""
     torch = _torch()
     lib = load_library()
     dev = _q_checks(q, w)

@@ -361,7 +361,9 @@ indexer_status indexer_score_topk_fused_prefill(const void *q, int64_t q_stride_
                                          n_tokens, n_pool, scores, row);
         if ((st = run_score(a, n_heads, head_dim, false, 1, s)) != INDEXER_OK) return st;
     }
-    return run_topk(scores, row, n_tokens, n_pool, nullptr, k_top, idx, val, out_stride, topk_ws, s);
+    // keys at or past vis_len[t] are -inf by definition: the top-k reads
+    // only each row's visible prefix
+    return run_topk(scores, row, n_tokens, n_pool, vis_len, k_top, idx, val, out_stride, topk_ws, s);
 }
 
 indexer_status indexer_score_topk_fused_decode(const void *q, int64_t q_stride_t, int64_t q_stride_h,

@@ -4,8 +4,8 @@
 // Order: score descending, equal scores by lower key index; -inf and NaN are
 // never selected; -0 ties with +0; short rows are padded with (-1, -inf).
 // Every score maps to an order-preserving 32-bit key (0 = not selectable);
-// values are re-read from the row so that they are reported exactly as
-// stored.  Three kernels, by row length:
+// reported values are the keys mapped back (a zero is re-read from the row,
+// so that -0 is reported as stored).  Three kernels, by row length:
 //  * rows of up to 16384 keys (topk_rows_kernel): one workgroup per row, the
 //    keys register-resident.  Fast path: one histogram of the 12 bits just
 //    below the common prefix of the row's largest and smallest selectable
@@ -39,6 +39,13 @@ __device__ __forceinline__ uint32_t order_key(float x) {
     if (u == 0xff800000u) return 0u;   // -inf: never selected
     if (u == 0x80000000u) u = 0u;      // -0 ties with +0
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// The score a selectable key stands for (order_key inverted).  +0 and -0
+// share a key, so a zero is read back from the row to report it as stored.
+__device__ __forceinline__ float key_value(uint32_t u, const float *row, int s) {
+    if (u == 0x80000000u) return row[s];
+    return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
 __device__ __forceinline__ unsigned long long lanes_below(int lane) {
@@ -206,7 +213,7 @@ __device__ void topk_row_general(const TopkArgs &a, int k_pad, unsigned char *sm
         if (j < total_sel) {
             const int s = (int)(~(uint32_t)(sel[j] & 0xffffffffull));
             idx_out[j] = s;
-            if (val_out) val_out[j] = row[s];
+            if (val_out) val_out[j] = key_value((uint32_t)(sel[j] >> 32), row, s);
         } else {
             idx_out[j] = -1;
             if (val_out) val_out[j] = -INFINITY;
@@ -341,7 +348,7 @@ __global__ void __launch_bounds__(kThreads, 1) topk_long_kernel(TopkArgs a, int 
     auto emit = [&](int pos, unsigned long long e) {
         const int s = (int)(~(uint32_t)(e & 0xffffffffull));
         idx_out[pos] = s;
-        if (val_out) val_out[pos] = row[s];
+        if (val_out) val_out[pos] = key_value((uint32_t)(e >> 32), row, s);
     };
     auto pack = [](int i, uint32_t u) {
         return ((unsigned long long)u << 32) | (uint32_t)(~(uint32_t)i);
@@ -691,7 +698,7 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
     auto emit = [&](int pos, unsigned long long e) {
         const int s = (int)(~(uint32_t)(e & 0xffffffffull));
         idx_out[pos] = s;
-        if (val_out) val_out[pos] = row[s];
+        if (val_out) val_out[pos] = key_value((uint32_t)(e >> 32), row, s);
     };
 
     // ---- fast path: one 12-bit histogram serves as both the select and the
