@@ -354,7 +354,9 @@ __global__ void __launch_bounds__(kThreads, 1) topk_long_kernel(TopkArgs a, int 
         return ((unsigned long long)u << 32) | (uint32_t)(~(uint32_t)i);
     };
 
-    // ---- 1. count, min, max -------------------------------------------------
+    // ---- 1. count, min, max, and a histogram of the keys' top 12 bits ------
+    for (int i = tid; i < 4096; i += kThreads) hist[i] = 0u;
+    __syncthreads();
     int cnt = 0;
     uint32_t mn = 0xffffffffu, mx = 0u;
     stream_row(row, n, [&](int, float x) {
@@ -363,6 +365,7 @@ __global__ void __launch_bounds__(kThreads, 1) topk_long_kernel(TopkArgs a, int 
             ++cnt;
             mn = min(mn, u);
             mx = max(mx, u);
+            atomicAdd(&hist[u >> 20], 1u);
         }
     });
 #pragma unroll
@@ -376,7 +379,6 @@ __global__ void __launch_bounds__(kThreads, 1) topk_long_kernel(TopkArgs a, int 
         sc[8 + kWaves + wid] = (int)mn;
         sc[8 + 2 * kWaves + wid] = (int)mx;
     }
-    for (int i = tid; i < 4096; i += kThreads) hist[i] = 0u;
     if (tid == 0) sc[3] = 0;
     __syncthreads();
     int nsel = 0;
@@ -396,30 +398,44 @@ __global__ void __launch_bounds__(kThreads, 1) topk_long_kernel(TopkArgs a, int 
     }
     if (nsel == 0) return;
 
-    // ---- 2. histogram below the common prefix, boundary bin ----------------
+    // ---- 2. boundary bin: of the top-12-bit histogram when its bin is small
+    // enough to gather, else of a second histogram of the 12 bits below the
+    // common prefix of the row's largest and smallest keys (the same bins
+    // when the row has keys of both signs) ---------------------------------
     int B = -1, shift = 0, nb = 1;
     if (!all) {
-        const int pos = 32 - __clz(mn ^ mx);
         if (mn == mx) {  // every selectable key equal: index order decides
             __syncthreads();
             topk_row_general(a, k_pad, smem);
             return;
         }
-        const int width = pos < 12 ? pos : 12;
-        shift = pos - width;
-        nb = 1 << width;
-        stream_row(row, n, [&](int, float x) {
-            const uint32_t u = order_key(x);
-            if (u) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
-        });
-        __syncthreads();
-        scan_bins_desc(hist, hcur, nb, k, sc);
-        B = sc[0];
-        const int cnt_b = sc[2];
-        if (cnt_b > kLongCand) {
+        scan_bins_desc(hist, hcur, 4096, k, sc);
+        const int cnt_top = sc[2];
+        __syncthreads();  // every thread has read sc[2] before it may change
+        if (cnt_top <= kLongCand) {
+            B = sc[0];
+            shift = 20;
+            nb = 4096;
+        } else {
+            const int pos = 32 - __clz(mn ^ mx);
+            const int width = pos < 12 ? pos : 12;
+            shift = pos - width;
+            nb = 1 << width;
+            for (int i = tid; i < 4096; i += kThreads) hist[i] = 0u;
             __syncthreads();
-            topk_row_general(a, k_pad, smem);
-            return;
+            stream_row(row, n, [&](int, float x) {
+                const uint32_t u = order_key(x);
+                if (u) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+            });
+            __syncthreads();
+            scan_bins_desc(hist, hcur, nb, k, sc);
+            B = sc[0];
+            const int cnt_b = sc[2];
+            if (cnt_b > kLongCand) {
+                __syncthreads();
+                topk_row_general(a, k_pad, smem);
+                return;
+            }
         }
     }
 
