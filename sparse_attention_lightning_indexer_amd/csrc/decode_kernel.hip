@@ -307,7 +307,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(ScoreArgs a) {
 // until an earlier one returns, and while it stalls it computes nothing.  So
 // the loads and the arithmetic run on different waves:
 //  * four producers (one per SIMD) fetch, for every tile, a quarter of its
-//    keys (16-byte direct-to-LDS loads into swizzled rows of a 3-deep ring),
+//    keys (16-byte direct-to-LDS loads into swizzled rows of a ring of 3 or
+//    4 tiles),
 //    its f16 mask rows when a mask is given (same loads, into a mask ring)
 //    and the tile's block ids three tiles ahead (4-byte
 //    direct-to-LDS loads into a small ring per producer); with one query row
