@@ -478,59 +478,104 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
     const int tid = threadIdx.x, wid = uni(tid >> 6), lane = tid & 63;
     const int m = lane & 31, kh = lane >> 5;
 
-    // keys visible to row t = req*Q + j of request req
-    auto row_vis = [=](int req, int t) {
-        return min(max(slen[req] - Q + 1 + (t - req * Q), 0), n_cols);
-    };
+    // keys visible to row t = req*Q + j of a request whose sequence holds sl keys
+    auto vis_of = [=](int sl, int req, int t) { return min(max(sl - Q + 1 + (t - req * Q), 0), n_cols); };
 
     // ---- 1. keys visible to each row group, tiles, prefix sum ------------
-    for (int r = tid; r < n_req; r += NT) slen[r] = max(0, seqp[r]);
-    if (tid < 32) misc[tid] = 0;
-    lds_barrier();
-    for (int e = tid; e < n_rg; e += NT) {
-        const int req = e / gpr, sub = e - (e / gpr) * gpr;
-        const int r0 = req * Q + sub * ROWS, r1 = min(req * Q + Q, r0 + ROWS);
-        gbd[e] = row_vis(req, r1 - 1);
-    }
-    lds_barrier();
-    {
-        const int per = (n_rg + NT - 1) / NT;
-        int local = 0;
-        for (int q = 0; q < per; ++q) {
-            const int e = tid * per + q;
-            if (e < n_rg) local += (gbd[e] + TK - 1) / TK;
+    // With at most 64 row groups and requests every wave works the split out
+    // itself, one row group (and one request) per lane, and later reads it
+    // back with readlane: no LDS arrays, and one barrier (for the flags),
+    // passed while the sequence lengths are on their way.  Otherwise the
+    // split goes through LDS.
+    const bool small = n_rg <= 64 && n_req <= 64;
+    int sl_l = 0, gbd_l = 0, pref_l = 0, tiles_l = 0, total_l = 0;
+    int64_t T;
+    int rg_first = 0;
+    if (small) {
+        int sl_g = 0;
+        if (lane < n_req) sl_l = max(0, seqp[lane]);
+        if (lane < n_rg) sl_g = max(0, seqp[lane / gpr]);
+        if (tid < 32) misc[tid] = 0;
+        lds_barrier();
+        if (lane < n_rg) {
+            const int req = lane / gpr, sub = lane - req * gpr;
+            const int r0 = req * Q + sub * ROWS, r1 = min(req * Q + Q, r0 + ROWS);
+            gbd_l = vis_of(sl_g, req, r1 - 1);
+            tiles_l = (gbd_l + TK - 1) / TK;
         }
-        int incl = local;
+        int incl = tiles_l;
         for (int o = 1; o < 64; o <<= 1) {
             const int y = __shfl_up(incl, o, 64);
             if (lane >= o) incl += y;
         }
-        if (lane == 63) misc[wid] = incl;
+        pref_l = incl - tiles_l;
+        total_l = __builtin_amdgcn_readlane(incl, 63);
+        T = total_l;
+    } else {
+        for (int r = tid; r < n_req; r += NT) slen[r] = max(0, seqp[r]);
+        if (tid < 32) misc[tid] = 0;
         lds_barrier();
-        int run = incl - local, total = 0;
-        for (int w = 0; w < NW; ++w) {
-            run += w < wid ? misc[w] : 0;
-            total += misc[w];
+        for (int e = tid; e < n_rg; e += NT) {
+            const int req = e / gpr, sub = e - (e / gpr) * gpr;
+            const int r0 = req * Q + sub * ROWS, r1 = min(req * Q + Q, r0 + ROWS);
+            gbd[e] = vis_of(slen[req], req, r1 - 1);
         }
-        for (int q = 0; q < per; ++q) {
-            const int e = tid * per + q;
-            if (e < n_rg) {
-                pref[e] = run;
-                run += (gbd[e] + TK - 1) / TK;
+        lds_barrier();
+        {
+            const int per = (n_rg + NT - 1) / NT;
+            int local = 0;
+            for (int q = 0; q < per; ++q) {
+                const int e = tid * per + q;
+                if (e < n_rg) local += (gbd[e] + TK - 1) / TK;
             }
+            int incl = local;
+            for (int o = 1; o < 64; o <<= 1) {
+                const int y = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += y;
+            }
+            if (lane == 63) misc[wid] = incl;
+            lds_barrier();
+            int run = incl - local, total = 0;
+            for (int w = 0; w < NW; ++w) {
+                run += w < wid ? misc[w] : 0;
+                total += misc[w];
+            }
+            for (int q = 0; q < per; ++q) {
+                const int e = tid * per + q;
+                if (e < n_rg) {
+                    pref[e] = run;
+                    run += (gbd[e] + TK - 1) / TK;
+                }
+            }
+            if (tid == 0) pref[n_rg] = total;
+            lds_barrier();
         }
-        if (tid == 0) pref[n_rg] = total;
-        lds_barrier();
+        T = uni(pref[n_rg]);
     }
-    const int64_t T = uni(pref[n_rg]);
     const int t_begin = (int)(T * blockIdx.x / gridDim.x);
     const int t_end = (int)(T * (blockIdx.x + 1) / gridDim.x);
     const int n_mine = t_end - t_begin;
-    if (n_mine > 0)
-        for (int e = tid; e < n_rg; e += NT)
-            if (pref[e] <= t_begin && t_begin < pref[e + 1]) misc[8] = e;
-    lds_barrier();
-    const int rg_first = n_mine > 0 ? uni(misc[8]) : 0;
+    if (small) {
+        const unsigned long long hit = __builtin_amdgcn_ballot_w64(
+            lane < n_rg && pref_l <= t_begin && t_begin < pref_l + tiles_l);
+        rg_first = n_mine > 0 ? (int)__builtin_ctzll(hit) : 0;
+    } else {
+        if (n_mine > 0)
+            for (int e = tid; e < n_rg; e += NT)
+                if (pref[e] <= t_begin && t_begin < pref[e + 1]) misc[8] = e;
+        lds_barrier();
+        rg_first = n_mine > 0 ? uni(misc[8]) : 0;
+    }
+    // the split, read back: first tile of row group e (e <= n_rg), keys
+    // visible to row group e, keys visible to row t of request req
+    auto pref_at = [&](int e) -> int {
+        if (small) return e >= n_rg ? total_l : __builtin_amdgcn_readlane(pref_l, e);
+        return uni(pref[e]);
+    };
+    auto gbd_at = [&](int e) -> int { return small ? __builtin_amdgcn_readlane(gbd_l, e) : uni(gbd[e]); };
+    auto row_vis = [&](int req, int t) {
+        return vis_of(small ? __builtin_amdgcn_readlane(sl_l, req) : slen[req], req, t);
+    };
 
     // per-tile cursor (wave-uniform): row group, its ordinal among this
     // workgroup's row groups, first key, keys visible to the group, and the
@@ -541,20 +586,20 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
         const int t_ = t_begin + (j);                        \
         if (t_ >= hi) {                                      \
             int e_ = rg + 1;                                 \
-            while (uni(pref[e_ + 1]) <= t_) ++e_;            \
+            while (pref_at(e_ + 1) <= t_) ++e_;              \
             ++ord;                                           \
             rg = e_;                                         \
-            lo = uni(pref[e_]);                              \
-            hi = uni(pref[e_ + 1]);                          \
-            bound = uni(gbd[e_]);                            \
+            lo = pref_at(e_);                                \
+            hi = pref_at(e_ + 1);                            \
+            bound = gbd_at(e_);                              \
         }                                                    \
         s0 = (t_ - lo) * TK;                                 \
     } while (0)
 
-    const int lo_first = n_mine > 0 ? uni(pref[rg_first]) : 0;
-    const int hi_first = n_mine > 0 ? uni(pref[rg_first + 1]) : 0;
+    const int lo_first = n_mine > 0 ? pref_at(rg_first) : 0;
+    const int hi_first = n_mine > 0 ? pref_at(rg_first + 1) : 0;
     const int s0_first = (t_begin - lo_first) * TK;
-    const int bd_first = n_mine > 0 ? uni(gbd[rg_first]) : 0;
+    const int bd_first = n_mine > 0 ? gbd_at(rg_first) : 0;
 
     if (wid >= NCONS) {
         // ================= producers =================
@@ -902,7 +947,7 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
 
     // ---- 2. -inf past the last tile of every row group (shared out) --------
     for (int e = blockIdx.x; e < n_rg; e += gridDim.x) {
-        const int lo = (uni(pref[e + 1]) - uni(pref[e])) * TK;
+        const int lo = (pref_at(e + 1) - pref_at(e)) * TK;
         if (lo >= n_cols) continue;
         const int req_ = e / gpr, sub_ = e - req_ * gpr;
         const int row0 = req_ * Q + sub_ * ROWS;
