@@ -807,6 +807,20 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
                 rvis[j] = tr < rhi ? row_vis(req_c, tr) : 0;
             }
         };
+        // -inf past the last tile of every row group (shared out over the
+        // workgroups; no tile writes there), while the first tile is on its way
+        for (int e = blockIdx.x; e < n_rg; e += gridDim.x) {
+            const int lo = (pref_at(e + 1) - pref_at(e)) * TK;
+            if (lo >= n_cols) continue;
+            const int req_ = e / gpr, sub_ = e - req_ * gpr;
+            const int row0 = req_ * Q + sub_ * ROWS;
+            const int nrows = min(req_ * Q + Q, row0 + ROWS) - row0;
+            const int width = n_cols - lo;
+            for (int c = tid; c < nrows * width; c += NCONS * 64) {
+                const int r = c / width;
+                scorep[(int64_t)(row0 + r) * score_st + lo + (c - r * width)] = -INFINITY;
+            }
+        }
         if constexpr (!QLDS) {
             // the first row group's q loads now, while its first tile is on its way
             if (n_mine > 0) {
@@ -944,20 +958,6 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
         (void)c_bd;
     }
 #undef LIDX_ADVANCE
-
-    // ---- 2. -inf past the last tile of every row group (shared out) --------
-    for (int e = blockIdx.x; e < n_rg; e += gridDim.x) {
-        const int lo = (pref_at(e + 1) - pref_at(e)) * TK;
-        if (lo >= n_cols) continue;
-        const int req_ = e / gpr, sub_ = e - req_ * gpr;
-        const int row0 = req_ * Q + sub_ * ROWS;
-        const int nrows = min(req_ * Q + Q, row0 + ROWS) - row0;
-        const int width = n_cols - lo;
-        for (int c = tid; c < nrows * width; c += NT) {
-            const int r = c / width;
-            scorep[(int64_t)(row0 + r) * score_st + lo + (c - r * width)] = -INFINITY;
-        }
-    }
 }
 
 template <int H, int D, bool SPLIT, int NC>
