@@ -67,6 +67,51 @@ __device__ __forceinline__ float relu(float x) {
     return __builtin_bit_cast(float, max(__builtin_bit_cast(int, x), 0));
 }
 
+// Wave-level sums, extrema and scans through DPP lane moves (VALU
+// operations; a 64-lane shuffle would take an LDS round trip per step).
+// Reductions: swap within quads, then mirror within half rows and rows, so
+// every lane of a 16-lane row holds the row's value; the four rows are then
+// combined from lanes 0, 16, 32 and 48 (a wave-uniform result).
+template <int CTRL, int ROWS = 0xf>
+__device__ __forceinline__ int dpp_move(int old, int v) {
+    return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xf, false);
+}
+template <typename OP>
+__device__ __forceinline__ int row_reduce(int v, int identity, OP op) {
+    v = op(v, dpp_move<0xb1>(identity, v));   // quad_perm [1,0,3,2]
+    v = op(v, dpp_move<0x4e>(identity, v));   // quad_perm [2,3,0,1]
+    v = op(v, dpp_move<0x141>(identity, v));  // row_half_mirror
+    v = op(v, dpp_move<0x140>(identity, v));  // row_mirror
+    return v;
+}
+__device__ __forceinline__ int wave_sum(int v) {
+    v = row_reduce(v, 0, [](int a, int b) { return a + b; });
+    return __builtin_amdgcn_readlane(v, 0) + __builtin_amdgcn_readlane(v, 16) +
+           __builtin_amdgcn_readlane(v, 32) + __builtin_amdgcn_readlane(v, 48);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t u) {
+    const int v = row_reduce((int)u, 0, [](int a, int b) { return (int)max((uint32_t)a, (uint32_t)b); });
+    return max(max((uint32_t)__builtin_amdgcn_readlane(v, 0), (uint32_t)__builtin_amdgcn_readlane(v, 16)),
+               max((uint32_t)__builtin_amdgcn_readlane(v, 32), (uint32_t)__builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t u) {
+    const int v = row_reduce((int)u, -1, [](int a, int b) { return (int)min((uint32_t)a, (uint32_t)b); });
+    return min(min((uint32_t)__builtin_amdgcn_readlane(v, 0), (uint32_t)__builtin_amdgcn_readlane(v, 16)),
+               min((uint32_t)__builtin_amdgcn_readlane(v, 32), (uint32_t)__builtin_amdgcn_readlane(v, 48)));
+}
+// Inclusive prefix sum over the wave's lanes: shifts by 1, 2, 4 and 8 inside
+// each 16-lane row, then the end of row 0 (and 2) into row 1 (and 3), then
+// the end of row 1 into rows 2 and 3.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+    v += dpp_move<0x111>(0, v);       // row_shr:1
+    v += dpp_move<0x112>(0, v);       // row_shr:2
+    v += dpp_move<0x114>(0, v);       // row_shr:4
+    v += dpp_move<0x118>(0, v);       // row_shr:8
+    v += dpp_move<0x142, 0xa>(0, v);  // row_bcast:15
+    v += dpp_move<0x143, 0xc>(0, v);  // row_bcast:31
+    return v;
+}
+
 __device__ __forceinline__ void wait_vmem_all() {
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 }

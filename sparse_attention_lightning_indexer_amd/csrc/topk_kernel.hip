@@ -19,6 +19,7 @@
 //  * topk_row_general: the fully general streaming fallback (heavy ties).
 #include <atomic>
 
+#include "device_common.h"
 #include "internal.h"
 
 #include <math.h>
@@ -56,12 +57,7 @@ __device__ __forceinline__ unsigned long long lanes_below(int lane) {
 // total.  `tmp` holds kWaves ints.  Contains two barriers.
 __device__ int block_exclusive_scan(int v, int *tmp, int &total) {
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-    }
+    const int incl = wave_incl_scan(v);
     if (lane == 63) tmp[wid] = incl;
     __syncthreads();
     int off = 0, tot = 0;
@@ -322,8 +318,7 @@ __device__ void scan_bins_desc(const uint32_t *h, uint32_t *start, int nb, int t
         }
         run += c[q];
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) fullmax = max(fullmax, __shfl_xor(fullmax, o, 64));
+    fullmax = (int)wave_max_u32((uint32_t)fullmax);
     if (lane == 0) sc[8 + wid] = fullmax;
     __syncthreads();
 }
@@ -368,12 +363,9 @@ __global__ void __launch_bounds__(kThreads, 1) topk_long_kernel(TopkArgs a, int 
             atomicAdd(&hist[u >> 20], 1u);
         }
     });
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        cnt += __shfl_xor(cnt, o, 64);
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
-    }
+    cnt = wave_sum(cnt);
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
     if (lane == 0) {
         sc[8 + wid] = cnt;
         sc[8 + kWaves + wid] = (int)mn;
@@ -454,11 +446,8 @@ __global__ void __launch_bounds__(kThreads, 1) topk_long_kernel(TopkArgs a, int 
         smn = min(smn, u);
         smx = max(smx, u);
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        smn = min(smn, (uint32_t)__shfl_xor((int)smn, o, 64));
-        smx = max(smx, (uint32_t)__shfl_xor((int)smx, o, 64));
-    }
+    smn = wave_min_u32(smn);
+    smx = wave_max_u32(smx);
     if (lane == 0) {
         sc[16 + wid] = (int)smn;
         sc[16 + kWaves + wid] = (int)smx;
@@ -573,12 +562,7 @@ template <int THREADS>
 __device__ __forceinline__ int scan_excl(int v, int *tmp, int &total) {
     constexpr int NW = THREADS / 64;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
-    int incl = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const int y = __shfl_up(incl, o, 64);
-        if (lane >= o) incl += y;
-    }
+    const int incl = wave_incl_scan(v);
     if (lane == 63) tmp[wid] = incl;
     __syncthreads();
     int off = 0, tot = 0;
@@ -614,8 +598,7 @@ __device__ void threshold_bin(const uint32_t *h, int nb, int need, int *sc) {
         }
     }
     int wsum = local;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) wsum += __shfl_xor(wsum, o, 64);
+    wsum = wave_sum(wsum);
     if (lane == 0) sc[4 + wid] = wsum;
     __syncthreads();
     // the wave whose bins contain the crossing, and the count before it
@@ -629,12 +612,7 @@ __device__ void threshold_bin(const uint32_t *h, int nb, int need, int *sc) {
         }
     }
     if (wid == wstar) {
-        int incl = local;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(local);
         int acc = before + incl - local;
 #pragma unroll
         for (int q = 0; q < MAXPER; ++q) {
@@ -687,12 +665,9 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
             mx = max(mx, key[j]);
         }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-        cnt += __shfl_xor(cnt, o, 64);
-        mn = min(mn, (uint32_t)__shfl_xor((int)mn, o, 64));
-        mx = max(mx, (uint32_t)__shfl_xor((int)mx, o, 64));
-    }
+    cnt = wave_sum(cnt);
+    mn = wave_min_u32(mn);
+    mx = wave_max_u32(mx);
     if (lane == 0) {
         sc[8 + wid] = cnt;
         sc[8 + NW + wid] = (int)mn;
@@ -772,8 +747,7 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
                 }
                 run += c[q];
             }
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) fullmax = max(fullmax, __shfl_xor(fullmax, o, 64));
+            fullmax = (int)wave_max_u32((uint32_t)fullmax);
             if (lane == 0) sc[8 + wid] = fullmax;
             if (tid == 0) sc[3] = 0;  // keys gathered from bin B
             __syncthreads();
@@ -888,12 +862,7 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
             v[q] = e < N ? table[e] : 0u;
             s += v[q];
         }
-        uint32_t incl = s;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            const uint32_t y = (uint32_t)__shfl_up((int)incl, o, 64);
-            if (lane >= o) incl += y;
-        }
+        const uint32_t incl = (uint32_t)wave_incl_scan((int)s);
         uint32_t run = incl - s;
 #pragma unroll
         for (int q = 0; q < PER; ++q) {
@@ -957,8 +926,7 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
             cmax = max(cmax, c4[q]);
         }
     }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) cmax = max(cmax, __shfl_xor(cmax, o, 64));
+    cmax = (int)wave_max_u32((uint32_t)cmax);
     if (lane == 0) sc[8 + wid] = cmax;
     int total;
     int run = scan_excl<THREADS>(local, sc + 64, total);  // its barriers publish sc[8..]
