@@ -503,11 +503,7 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
             gbd_l = vis_of(sl_g, req, r1 - 1);
             tiles_l = (gbd_l + TK - 1) / TK;
         }
-        int incl = tiles_l;
-        for (int o = 1; o < 64; o <<= 1) {
-            const int y = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += y;
-        }
+        const int incl = wave_incl_scan(tiles_l);
         pref_l = incl - tiles_l;
         total_l = __builtin_amdgcn_readlane(incl, 63);
         T = total_l;
@@ -528,11 +524,7 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
                 const int e = tid * per + q;
                 if (e < n_rg) local += (gbd[e] + TK - 1) / TK;
             }
-            int incl = local;
-            for (int o = 1; o < 64; o <<= 1) {
-                const int y = __shfl_up(incl, o, 64);
-                if (lane >= o) incl += y;
-            }
+            const int incl = wave_incl_scan(local);
             if (lane == 63) misc[wid] = incl;
             lds_barrier();
             int run = incl - local, total = 0;
