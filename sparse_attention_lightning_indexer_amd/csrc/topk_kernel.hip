@@ -577,6 +577,12 @@ __device__ __forceinline__ int scan_excl(int v, int *tmp, int &total) {
     return off + incl - v;
 }
 
+// Histogram bins of the row kernel: 4096 (12-bit digits) with 1024 threads;
+// 2048 (11-bit digits) with 512 threads, so that three workgroups (rows)
+// fit in a compute unit's LDS.
+constexpr int rows_bits(int threads) { return threads == 512 ? 11 : 12; }
+constexpr int rows_bins(int threads) { return 1 << rows_bits(threads); }
+
 // Finds, over nb bins read in descending order, the bin where the running
 // count first reaches `need`.  Returns (bin, need within the bin, bin count)
 // through sc[0..2]; ends with a barrier.  Uses sc[4..4+NW).
@@ -584,7 +590,7 @@ template <int THREADS>
 __device__ void threshold_bin(const uint32_t *h, int nb, int need, int *sc) {
     constexpr int NW = THREADS / 64;
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    constexpr int MAXPER = 4096 / THREADS;
+    constexpr int MAXPER = rows_bins(THREADS) / THREADS;
     const int per = nb > THREADS ? nb / THREADS : 1;  // bins per thread
     int c[MAXPER];
     int local = 0;
@@ -630,14 +636,16 @@ __device__ void threshold_bin(const uint32_t *h, int nb, int need, int *sc) {
 template <int THREADS, int E>
 __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) {
     constexpr int NW = THREADS / 64;
-    // LDS: hist0 | hist1 (16 KB each) | sel | tmp (p2*8 each) | table | scalars
+    constexpr int BITS = rows_bits(THREADS), NBINS = rows_bins(THREADS);
+    constexpr int HB = 4 * NBINS;  // bytes of one histogram
+    // LDS: hist0 | hist1 (HB each) | sel | tmp (p2*8 each) | table | scalars
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint32_t *hist0 = reinterpret_cast<uint32_t *>(smem);
-    uint32_t *hist1 = reinterpret_cast<uint32_t *>(smem + 16384);
-    unsigned long long *sel = reinterpret_cast<unsigned long long *>(smem + 32768);
-    unsigned long long *tmp = reinterpret_cast<unsigned long long *>(smem + 32768 + 8 * (size_t)p2);
-    uint32_t *table = reinterpret_cast<uint32_t *>(smem + 32768 + 16 * (size_t)p2);
-    int *sc = reinterpret_cast<int *>(smem + 32768 + 16 * (size_t)p2 + 4 * E * NW);
+    uint32_t *hist1 = reinterpret_cast<uint32_t *>(smem + HB);
+    unsigned long long *sel = reinterpret_cast<unsigned long long *>(smem + 2 * HB);
+    unsigned long long *tmp = reinterpret_cast<unsigned long long *>(smem + 2 * HB + 8 * (size_t)p2);
+    uint32_t *table = reinterpret_cast<uint32_t *>(smem + 2 * HB + 16 * (size_t)p2);
+    int *sc = reinterpret_cast<int *>(smem + 2 * HB + 16 * (size_t)p2 + 4 * E * NW);
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int t = blockIdx.x;
@@ -652,7 +660,7 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
         const int i = tid + THREADS * j;
         key[j] = i < n ? order_key(row[i]) : 0u;
     }
-    for (int i = tid; i < 4096; i += THREADS) hist0[i] = 0u;
+    for (int i = tid; i < NBINS; i += THREADS) hist0[i] = 0u;
 
     // ---- count, min and max of the selectable keys ---------------------
     int cnt = 0;
@@ -705,7 +713,7 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
         const uint32_t diff = mn ^ mx;
         const int pos = diff ? 32 - __clz(diff) : 0;
         if (nsel > 0 && pos > 0) {
-            const int width = pos < 12 ? pos : 12;
+            const int width = pos < BITS ? pos : BITS;
             const int shift = pos - width;
             const int nb = 1 << width;
             const bool all0 = nsel <= k;
@@ -715,7 +723,7 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
                 if (key[j]) atomicAdd(&hist0[(key[j] >> shift) & (nb - 1)], 1u);
             __syncthreads();
             // descending exclusive scan of the bin counts
-            constexpr int MAXPER = 4096 / THREADS;
+            constexpr int MAXPER = NBINS / THREADS;
             const int per = nb > THREADS ? nb / THREADS : 1;
             int c[MAXPER];
             int local = 0;
@@ -797,7 +805,7 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
                 return;
             }
             // general path: clear what the fast path used
-            for (int i = tid; i < 4096; i += THREADS) hist0[i] = 0u;
+            for (int i = tid; i < NBINS; i += THREADS) hist0[i] = 0u;
             __syncthreads();
         }
     }
@@ -813,7 +821,7 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
         prefix = mx & pmask;
         int pass = 0;
         while (pos > 0) {
-            const int width = pos < 12 ? pos : 12;
+            const int width = pos < BITS ? pos : BITS;
             const int shift = pos - width;
             const int nb = 1 << width;
             uint32_t *h = (pass & 1) ? hist1 : hist0;
@@ -823,7 +831,7 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
                 const uint32_t u = key[j];
                 if (u && (u & pmask) == prefix) atomicAdd(&h[(u >> shift) & (nb - 1)], 1u);
             }
-            for (int i = tid; i < 4096; i += THREADS) hn[i] = 0u;  // next pass
+            for (int i = tid; i < NBINS; i += THREADS) hn[i] = 0u;  // next pass
             __syncthreads();
             threshold_bin<THREADS>(h, nb, need, sc);
             const uint32_t digit = (uint32_t)sc[0];
@@ -874,7 +882,7 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
     // bucket histogram of the next phase lives in hist0/hist1's free buffer
     uint32_t *bh = hist0;
     uint32_t *bstart = hist1;
-    for (int i = tid; i < 4096; i += THREADS) bh[i] = 0u;
+    for (int i = tid; i < NBINS; i += THREADS) bh[i] = 0u;
     __syncthreads();
 #pragma unroll
     for (int j = 0; j < E; ++j) {
@@ -906,13 +914,13 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
         return;
     }
     const int pos2 = 32 - __clz(d2);
-    const int bshift = pos2 > 12 ? pos2 - 12 : 0;
+    const int bshift = pos2 > BITS ? pos2 - BITS : 0;
     const int bnb = 1 << (pos2 - bshift);
     for (int j = tid; j < total_sel; j += THREADS)
         atomicAdd(&bh[(uint32_t)(sel[j] >> (32 + bshift)) & (bnb - 1)], 1u);
     __syncthreads();
     // descending exclusive scan of bucket counts -> start offsets; max count
-    constexpr int MAXPER = 4096 / THREADS;
+    constexpr int MAXPER = NBINS / THREADS;
     const int per = bnb > THREADS ? bnb / THREADS : 1;
     int c4[MAXPER];
     int local = 0, cmax = 0;
@@ -987,7 +995,7 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
 
 template <int THREADS, int E>
 size_t rows_lds_bytes(int p2) {
-    return 32768 + 16 * (size_t)p2 + 4 * (size_t)E * (THREADS / 64) + 4 * (64 + THREADS / 64) + 16;
+    return 8 * (size_t)rows_bins(THREADS) + 16 * (size_t)p2 + 4 * (size_t)E * (THREADS / 64) + 4 * (64 + THREADS / 64) + 16;
 }
 
 template <int THREADS, int E>
@@ -1011,8 +1019,8 @@ hipError_t launch_topk(const TopkArgs &a, void *, hipStream_t stream) {
     int k_pad = 1;
     while (k_pad < a.k_top) k_pad <<= 1;
     const int n = a.n_cols;
-    // many rows: 512-thread workgroups so that two rows share a compute unit;
-    // few rows: 1024 threads per row for the shortest latency
+    // many rows: 512-thread workgroups so that three rows share a compute
+    // unit; few rows: 1024 threads per row for the shortest latency
     const bool many = a.n_rows >= 2 * device_cu_count();
     if (many && n <= 512 * 16) {
         if (n <= 512 * 2) return launch_rows<512, 2>(a, k_pad, stream);
