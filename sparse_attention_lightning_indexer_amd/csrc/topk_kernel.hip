@@ -20,6 +20,7 @@
 #include <atomic>
 
 #include "device_common.h"
+#include "indexer.h"
 #include "internal.h"
 
 #include <math.h>
@@ -219,14 +220,16 @@ __device__ void topk_row_general(const TopkArgs &a, int k_pad, unsigned char *sm
 
 // ---------------------------------------------------------------------------
 // Long rows (more keys than the register-resident kernel holds): one
-// workgroup per row streams the row three times and never orders it there.
-//  1. count and min/max of the selectable keys;
-//  2. a histogram of the 12 bits just below the common prefix of min and
-//     max (which spreads the keys over many bins, so LDS atomics rarely
-//     collide), whose descending scan gives the bin B holding the k-th key;
+// workgroup per row, two per compute unit, streams the row twice (three
+// times when the first histogram is too coarse) and never orders it there.
+//  1. count, min/max of the selectable keys and a histogram of their top 12
+//     bits, whose descending scan gives the bin B holding the k-th key;
+//  2. when B holds more than kLongCand keys, a histogram of the 12 bits just
+//     below the common prefix of min and max instead (which spreads the
+//     keys over many bins);
 //  3. every key of a bin >= B is gathered into LDS (at most k plus the
 //     kLongCand keys of B).
-// The gathered set is then selected and ordered in LDS: a second 12-bit
+// The gathered set is then selected and ordered in LDS: an 11-bit
 // histogram below the set's own common prefix gives every bin its output
 // offset and the bin holding the last selected position; keys of higher bins
 // go to their bin's range and are placed by their rank inside it, keys of
@@ -237,12 +240,16 @@ __device__ void topk_row_general(const TopkArgs &a, int k_pad, unsigned char *sm
 // ---------------------------------------------------------------------------
 
 constexpr int kMaxBucket = 64;     // largest bin ordered by ranking inside it
-constexpr int kLongCand = 4096;
-constexpr int kLongS = 8192;       // gathered-set capacity (a power of two >= k + kLongCand)
+constexpr int kLongCand = 2048;
+constexpr int kLongS = 4096;       // gathered-set capacity (a power of two >= k + kLongCand)
+static_assert(INDEXER_MAX_K_TOP + kLongCand <= kLongS, "gathered set");
 constexpr int kLongCand2 = 512;    // boundary-bin keys ranked directly in the final ordering
 
+// LDS: one 4096-bin histogram (the gathered set's 2048-bin histogram and
+// bin cursors reuse it), the gathered set, the ordered output, the boundary
+// bin's keys, scalars.  About 68 KB for k = 2048: two rows per compute unit.
 size_t long_lds_bytes(int k_pad) {
-    return 32768 + 8 * (size_t)kLongS + 8 * (size_t)k_pad + 8 * (size_t)kLongCand2 + 4 * 128;
+    return 16384 + 8 * (size_t)kLongS + 8 * (size_t)k_pad + 8 * (size_t)kLongCand2 + 4 * 128;
 }
 
 // Calls f(index, value) for every key of the row; 16-byte loads, four per
@@ -282,7 +289,7 @@ __device__ __forceinline__ void stream_row(const float *row, int n, F &&f) {
 
 // Descending exclusive scan of nb <= 4096 bin counts (each thread owns
 // 4096 / kThreads consecutive bins from the top).  Writes every bin's offset
-// to start[] and reports the bin holding position `total_sel - 1` in
+// to start[] (unless it is null) and reports the bin holding position `total_sel - 1` in
 // sc[0..2] (bin, keys to take from it, its count) and, in sc[8 + wave], the
 // largest bin above it.  Ends with a barrier.
 __device__ void scan_bins_desc(const uint32_t *h, uint32_t *start, int nb, int total_sel, int *sc) {
@@ -307,7 +314,7 @@ __device__ void scan_bins_desc(const uint32_t *h, uint32_t *start, int nb, int t
     for (int q = 0; q < MAXPER; ++q) {
         const int r = tid * per + q;
         if (q < per && r < nb) {
-            start[nb - 1 - r] = (uint32_t)run;
+            if (start) start[nb - 1 - r] = (uint32_t)run;
             if (run < total_sel && run + c[q] >= total_sel) {
                 sc[0] = nb - 1 - r;
                 sc[1] = total_sel - run;
@@ -323,11 +330,11 @@ __device__ void scan_bins_desc(const uint32_t *h, uint32_t *start, int nb, int t
     __syncthreads();
 }
 
-__global__ void __launch_bounds__(kThreads, 1) topk_long_kernel(TopkArgs a, int k_pad) {
+__global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int k_pad) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint32_t *hist = reinterpret_cast<uint32_t *>(smem);
-    uint32_t *hcur = reinterpret_cast<uint32_t *>(smem + 16384);
-    unsigned long long *S = reinterpret_cast<unsigned long long *>(smem + 32768);
+    uint32_t *hcur = hist + 2048;  // the gathered set's bin cursors (its histogram has <= 2048 bins)
+    unsigned long long *S = reinterpret_cast<unsigned long long *>(smem + 16384);
     unsigned long long *O = S + kLongS;
     unsigned long long *cand2 = O + k_pad;
     int *sc = reinterpret_cast<int *>(cand2 + kLongCand2);
@@ -401,7 +408,7 @@ __global__ void __launch_bounds__(kThreads, 1) topk_long_kernel(TopkArgs a, int 
             topk_row_general(a, k_pad, smem);
             return;
         }
-        scan_bins_desc(hist, hcur, 4096, k, sc);
+        scan_bins_desc(hist, nullptr, 4096, k, sc);
         const int cnt_top = sc[2];
         __syncthreads();  // every thread has read sc[2] before it may change
         if (cnt_top <= kLongCand) {
@@ -420,7 +427,7 @@ __global__ void __launch_bounds__(kThreads, 1) topk_long_kernel(TopkArgs a, int 
                 if (u) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
             });
             __syncthreads();
-            scan_bins_desc(hist, hcur, nb, k, sc);
+            scan_bins_desc(hist, nullptr, nb, k, sc);
             B = sc[0];
             const int cnt_b = sc[2];
             if (cnt_b > kLongCand) {
@@ -465,7 +472,7 @@ __global__ void __launch_bounds__(kThreads, 1) topk_long_kernel(TopkArgs a, int 
     bool sorted_out = false;
     if (smn != smx) {
         const int pos2 = 32 - __clz(smn ^ smx);
-        const int width2 = pos2 < 12 ? pos2 : 12;
+        const int width2 = pos2 < 11 ? pos2 : 11;
         const int shift2 = pos2 - width2;
         const int nb2 = 1 << width2;
         for (int q = tid; q < m; q += kThreads)
