@@ -589,6 +589,11 @@ __device__ __forceinline__ int scan_excl(int v, int *tmp, int &total) {
 // fit in a compute unit's LDS.
 constexpr int rows_bits(int threads) { return threads == 512 ? 11 : 12; }
 constexpr int rows_bins(int threads) { return 1 << rows_bits(threads); }
+// Capacity of the row kernel's tmp[] (keys of the boundary bin; the
+// bucketed ordering of the general path): 512 keys with 512 threads, so
+// that four rows fit in a compute unit's LDS (the general path then orders
+// larger sets with the bitonic sort), else the padded k.
+constexpr int rows_tmp_cap(int threads) { return threads == 512 ? 512 : 1 << 30; }
 
 // Finds, over nb bins read in descending order, the bin where the running
 // count first reaches `need`.  Returns (bin, need within the bin, bin count)
@@ -641,18 +646,19 @@ __device__ void threshold_bin(const uint32_t *h, int nb, int need, int *sc) {
 }
 
 template <int THREADS, int E>
-__global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) {
+__global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_kernel(TopkArgs a, int p2) {
     constexpr int NW = THREADS / 64;
     constexpr int BITS = rows_bits(THREADS), NBINS = rows_bins(THREADS);
     constexpr int HB = 4 * NBINS;  // bytes of one histogram
-    // LDS: hist0 | hist1 (HB each) | sel | tmp (p2*8 each) | table | scalars
+    const int tcap = min(p2, rows_tmp_cap(THREADS));
+    // LDS: hist0 | hist1 (HB each) | sel (p2*8) | tmp (tcap*8) | table | scalars
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint32_t *hist0 = reinterpret_cast<uint32_t *>(smem);
     uint32_t *hist1 = reinterpret_cast<uint32_t *>(smem + HB);
     unsigned long long *sel = reinterpret_cast<unsigned long long *>(smem + 2 * HB);
     unsigned long long *tmp = reinterpret_cast<unsigned long long *>(smem + 2 * HB + 8 * (size_t)p2);
-    uint32_t *table = reinterpret_cast<uint32_t *>(smem + 2 * HB + 16 * (size_t)p2);
-    int *sc = reinterpret_cast<int *>(smem + 2 * HB + 16 * (size_t)p2 + 4 * E * NW);
+    uint32_t *table = reinterpret_cast<uint32_t *>(smem + 2 * HB + 8 * (size_t)(p2 + tcap));
+    int *sc = reinterpret_cast<int *>(smem + 2 * HB + 8 * (size_t)(p2 + tcap) + 4 * E * NW);
 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int t = blockIdx.x;
@@ -955,7 +961,7 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
 #pragma unroll
     for (int w = 0; w < NW; ++w) bmax = max(bmax, sc[8 + w]);
 
-    if (bmax <= kMaxBucket) {
+    if (bmax <= kMaxBucket && total_sel <= tcap) {
         // scatter into buckets (order inside a bucket arbitrary), then rank
         for (int i = tid; i < bnb; i += THREADS) bh[i] = 0u;  // reuse as cursors
         __syncthreads();
@@ -1002,7 +1008,7 @@ __global__ void __launch_bounds__(THREADS) topk_rows_kernel(TopkArgs a, int p2) 
 
 template <int THREADS, int E>
 size_t rows_lds_bytes(int p2) {
-    return 8 * (size_t)rows_bins(THREADS) + 16 * (size_t)p2 + 4 * (size_t)E * (THREADS / 64) + 4 * (64 + THREADS / 64) + 16;
+    return 8 * (size_t)rows_bins(THREADS) + 8 * (size_t)(p2 + min(p2, rows_tmp_cap(THREADS))) + 4 * (size_t)E * (THREADS / 64) + 4 * (64 + THREADS / 64) + 16;
 }
 
 template <int THREADS, int E>
@@ -1026,7 +1032,7 @@ hipError_t launch_topk(const TopkArgs &a, void *, hipStream_t stream) {
     int k_pad = 1;
     while (k_pad < a.k_top) k_pad <<= 1;
     const int n = a.n_cols;
-    // many rows: 512-thread workgroups so that three rows share a compute
+    // many rows: 512-thread workgroups so that four rows share a compute
     // unit; few rows: 1024 threads per row for the shortest latency
     const bool many = a.n_rows >= 2 * device_cu_count();
     if (many && n <= 512 * 16) {

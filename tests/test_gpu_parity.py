@@ -356,6 +356,22 @@ def test_topk_selection_ends_at_a_bin_edge(n_rows):
         check_topk_exact(gi, gv, s, k, where=f"bin edge rows={n_rows} k={k}")
 
 
+
+def test_topk_many_rows_heavy_ties():
+    """Enough rows for the 512-thread launch shape (four rows per CU), with
+    scores drawn from a few values: crowded bins take the general path,
+    whose ordering of more than 512 selected keys is the bitonic sort, and
+    equal scores are ordered by index."""
+    rng = np.random.default_rng(11)
+    n_rows, n = 600, 5000
+    s = rng.integers(0, 7, size=(n_rows, n)).astype(np.float32)
+    s[rng.random(s.shape) < 0.1] = -np.inf
+    s[:4] = 3.0                                   # rows of one value
+    for k in (100, 600, 2048):
+        gi, gv = gpu_topk(dev(s), k)
+        check_topk_exact(gi, gv, s, k, where=f"heavy ties rows={n_rows} k={k}")
+
+
 # ------------------------------------------------------------ full workloads
 
 def _sampled_check(inp, rows, where):
