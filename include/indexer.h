@@ -127,7 +127,9 @@ indexer_status indexer_score_prefill(
  *                k_cache + ((int64)block_table[r*bt_stride + s/block_size]
  *                           * block_size + s % block_size) * k_stride_s
  *   block_table  i32 [n_requests][bt_stride]; only entries of keys
- *                s < min(seq_lens[r], max_seq_len) are read
+ *                s < min(seq_lens[r], max_seq_len) are used, but any entry
+ *                of the first ceil(max_seq_len / block_size) columns may be
+ *                loaded (to warm the cache), so all of them must be readable
  *   seq_lens     i32 [n_requests] keys per request (device memory)
  *   max_seq_len  width of the score rows; keys at or past it are ignored
  *   mask         f16 [n_requests*query_len][max_seq_len] (stride

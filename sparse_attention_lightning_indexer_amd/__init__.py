@@ -173,7 +173,7 @@ def score_prefill(q, k, w, mask=None, vis_len=None, out=None):
     return out
 
 
-def _paged_checks(q, k_cache, block_table, seq_lens, dev):
+def _paged_checks(q, k_cache, block_table, seq_lens, dev, max_seq_len):
     torch = _torch()
     _need(k_cache, "k_cache", torch.float16, dev, 3)
     _need(block_table, "block_table", torch.int32, dev, 2)
@@ -183,6 +183,10 @@ def _paged_checks(q, k_cache, block_table, seq_lens, dev):
         raise ValueError("k_cache must be [n_blocks, block_size, d] with contiguous slots")
     if block_table.stride(1) != 1:
         raise ValueError("block_table rows must be contiguous")
+    need = -(-max_seq_len // bs) if bs > 0 else 0
+    if block_table.shape[0] < seq_lens.shape[0] or block_table.shape[1] < need:
+        raise ValueError(f"block_table must be at least [n_requests, ceil(max_seq_len/block_size)] = "
+                         f"[{seq_lens.shape[0]}, {need}], got {tuple(block_table.shape)}")
     if not seq_lens.is_contiguous():
         raise ValueError("seq_lens must be contiguous")
     return bs
@@ -197,7 +201,7 @@ def score_decode(q, k_cache, block_table, seq_lens, query_len: int,
     lib = load_library()
     dev = _q_checks(q, w)
     RQ, H, d = q.shape
-    bs = _paged_checks(q, k_cache, block_table, seq_lens, dev)
+    bs = _paged_checks(q, k_cache, block_table, seq_lens, dev, max_seq_len)
     R = seq_lens.shape[0]
     if RQ != R * query_len:
         raise ValueError(f"q has {RQ} rows, expected n_requests*query_len = {R * query_len}")
@@ -305,7 +309,7 @@ def score_topk_fused_decode(q, k_cache, block_table, seq_lens, query_len: int,
     lib = load_library()
     dev = _q_checks(q, w)
     RQ, H, d = q.shape
-    bs = _paged_checks(q, k_cache, block_table, seq_lens, dev)
+    bs = _paged_checks(q, k_cache, block_table, seq_lens, dev, max_seq_len)
     R = seq_lens.shape[0]
     if RQ != R * query_len:
         raise ValueError(f"q has {RQ} rows, expected n_requests*query_len = {R * query_len}")

@@ -311,7 +311,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(ScoreArgs a) {
 //    4 tiles),
 //    its f16 mask rows when a mask is given (same loads, into a mask ring)
 //    and the tile's block ids three tiles ahead (4-byte
-//    direct-to-LDS loads into a small ring per producer); with one query row
+//    direct-to-LDS loads into a small ring per producer, issued behind the
+//    loads of the current tile); with one query row
 //    per request also the q row of each new row group (fragment order, one
 //    of two LDS slots).  A producer issues only direct-to-LDS loads, so
 //    exact vmcnt counts tell when its part of a tile has landed; it then
@@ -488,13 +489,36 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
     // passed while the sequence lengths are on their way.  Otherwise the
     // split goes through LDS.
     const bool small = n_rg <= 64 && n_req <= 64;
+    // The producers read the block table only once the split is known: a
+    // dependent round trip before the first key load.  While the sequence
+    // lengths are on their way, every lane loads one table entry, so that
+    // together the workgroups of one XCD (blockIdx.x mod 8) bring the table
+    // rows' first ceil(n_cols / block_size) entries into that XCD's L2 (up
+    // to one entry per thread of a workgroup).  The values are not used;
+    // the index is clamped, not branched on, so the load stays in straight
+    // code and waiting for the lengths does not wait for it, and every entry
+    // loaded lies inside the [n_req][bt_stride] table (n_req >= 1).
+    int bt_warm;
+    auto warm_block_table = [&]() {
+        const int nbm = sh >= 0 ? (n_cols + bs - 1) >> sh : (n_cols + bs - 1) / bs;
+        const int n_e = (int)min((int64_t)n_req * nbm, (int64_t)0x7fffffff);
+        const int per_xcd = (int)((gridDim.x + 7) / 8);
+        const int csz = min((n_e + per_xcd - 1) / per_xcd, NT);
+        const int e = min((int)(blockIdx.x / 8 % per_xcd) * csz + min(tid, csz - 1), n_e - 1);
+        const int r = (int)((unsigned)e / (unsigned)nbm);
+        bt_warm = btab[(int64_t)r * bt_stride + (e - r * nbm)];
+    };
     int sl_l = 0, gbd_l = 0, pref_l = 0, tiles_l = 0, total_l = 0;
     int64_t T;
     int rg_first = 0;
     if (small) {
-        int sl_g = 0;
-        if (lane < n_req) sl_l = max(0, seqp[lane]);
-        if (lane < n_rg) sl_g = max(0, seqp[lane / gpr]);
+        // one load per lane (n_req >= 1), the warming load behind it, then
+        // the wait; a row group's length comes from its request's lane
+        const int sl_raw = seqp[min(lane, n_req - 1)];
+        warm_block_table();
+        asm volatile("" ::"v"(sl_raw) : "memory");  // wait for the lengths here, after both loads are issued
+        sl_l = lane < n_req ? max(0, sl_raw) : 0;
+        const int sl_g = __builtin_amdgcn_ds_bpermute((lane / gpr) << 2, sl_l);
         if (tid < 32) misc[tid] = 0;
         lds_barrier();
         if (lane < n_rg) {
@@ -509,6 +533,7 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
         T = total_l;
     } else {
         for (int r = tid; r < n_req; r += NT) slen[r] = max(0, seqp[r]);
+        warm_block_table();
         if (tid < 32) misc[tid] = 0;
         lds_barrier();
         for (int e = tid; e < n_rg; e += NT) {
@@ -639,8 +664,10 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
 
         for (int j = 0; j < n_mine; ++j) {
             if (j > 0) LIDX_ADVANCE(k_rg, k_ord, k_s0, k_bd, k_lo, k_hi, j);
-            LIDX_ISSUE_BT(j + kBtLead);
-            wait_vmem_below(issued - mbt0);  // block ids of tile j are in LDS
+            // the block ids of tile j: already in flight except for the first
+            // tile (the look-ahead loads go out behind each tile's own loads,
+            // so the first tile's keys wait for one block-id load only)
+            LIDX_ISSUE_BT(j);
 
             // the ring slot of tile j last held tile j - NBUF; a new row
             // group's q slot last held the group two back
@@ -678,6 +705,7 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
                 gf1 = j;
                 last_ord = k_ord;
             }
+            wait_vmem_below(issued - mbt0);  // block ids of tile j are in LDS
 
             // keys of tile j; keys past the group's bound repeat its last
             // visible key (their scores are discarded), so every address is a
@@ -732,6 +760,8 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
                     ++issued;
                 }
             }
+            const int mk_now = issued;  // the last load of tile j
+            LIDX_ISSUE_BT(j + kBtLead);
             mbt0 = mbt1;
             mbt1 = mbt2;
             mbt2 = mbt3;
@@ -748,7 +778,7 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
                 }
             }
             mk2 = mk1;
-            mk1 = issued;
+            mk1 = mk_now;
         }
         if (n_mine > 0) {
             wait_vmem_all();
@@ -949,6 +979,7 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
         }
         (void)c_bd;
     }
+    asm volatile("" ::"v"(bt_warm));  // the warming load has returned before the wave ends
 #undef LIDX_ADVANCE
 }
 

@@ -253,6 +253,26 @@ def test_decode_wider_rows_than_lengths():
     _full_check(inp, inp.name)
 
 
+def test_decode_block_table_width():
+    """A block table with spare columns (row stride past ceil(max_seq_len /
+    block_size)) gives the same scores bit for bit; one narrower than that
+    is refused by the binding before any kernel runs (the kernel may load
+    any entry of those columns)."""
+    inp = W.random_decode(44, 5, 1, 64, 128, 16, 30, 300, 16)
+    ref = gpu_score(inp).cpu().numpy()
+    bt = inp.block_table
+    wide = np.full((bt.shape[0], bt.shape[1] + 7), 12345, np.int32)
+    wide[:, : bt.shape[1]] = bt
+    q, kc, sl, w = dev(inp.q), dev(inp.k_cache), dev(inp.seq_lens), dev(inp.w)
+    got = li.score_decode(q, kc, dev(wide), sl, inp.Q, inp.max_seq_len, w).cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+    narrow = dev(np.ascontiguousarray(bt[:, :-1]))
+    with pytest.raises(ValueError, match="block_table"):
+        li.score_decode(q, kc, narrow, sl, inp.Q, inp.max_seq_len, w)
+    with pytest.raises(ValueError, match="block_table"):
+        li.score_topk_fused_decode(q, kc, narrow, sl, inp.Q, inp.max_seq_len, w, inp.k_top)
+
+
 def test_paged_equals_contiguous():
     """The same keys through a permuted and an in-order block table give
     bit-identical scores, and agree with the contiguous layout (query j
