@@ -7,15 +7,19 @@ One step is the whole hot path over one batch of synthetic input.  Paged
 keys (decode, spec_decode) go through the fused entry point (the score
 kernel into a workspace, then the per-row top-k kernel); contiguous keys run
 the score into a [rows, keys] f32 buffer, then the per-row top-k.  The timed region is exactly K steps
-between two synchronisations; inputs are resident in HBM before it starts,
-and several copies of them are rotated so that consecutive steps do not hit
-the 256 MB Infinity Cache.
+between two synchronisations: by default one replay of a HIP graph captured
+from the K steps' calls (so the Python binding's per-call cost is not
+timed; the replay's last outputs are checked bit for bit against the same
+step issued eagerly, and the eager rate is reported beside it), with
+--eager the K calls themselves.  Inputs are resident in HBM before it
+starts, and several copies of them are rotated so that consecutive steps do
+not hit the 256 MB Infinity Cache.
 
 Prints ONE JSON line: throughput in visible (token, key) pairs per second,
 the roofline of the dominant kernel (its average duration measured with HIP
-events on the launch stream over its own timed loop; also the score and
-top-k kernels on their own), and the CPU oracle timed on a bounded sample of
-the same workload as a baseline.
+events on the launch stream over its own timed loop of K launches, replayed
+the same way; also the score and top-k kernels on their own), and the CPU
+oracle timed on a bounded sample of the same workload as a baseline.
 
 Workloads (``--config``):
   tiny            16 tokens x 256 keys, 4 heads of 64, top-32
@@ -175,6 +179,9 @@ def parse():
                     help="print the kernel table of a rocprofv3 --kernel-trace --stats run and exit")
     ap.add_argument("--no-peak-probe", action="store_true",
                     help="skip the measured-peak probes reported beside the published peak")
+    ap.add_argument("--eager", action="store_true",
+                    help="time the steps (and kernels) as Python-issued launches instead of one replay of a "
+                         "captured HIP graph of them")
     ap.add_argument("--no-kernel-split", action="store_true",
                     help="skip the separate score and top-k timing loops (and the roofline)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
@@ -304,37 +311,73 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
+    # A HIP graph of n launches of fn(i), captured on a side stream (the
+    # library launches on torch's current stream, which capture redirects);
+    # the library allocates nothing and records no memset, so replays
+    # repeat the same kernels on the same buffers.
+    def capture(fn, n):
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                for i in range(n):
+                    fn(i)
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g.replay()  # untimed: the first replay uploads the graph
+        torch.cuda.synchronize()
+        return g
+
+    def timed(fn, n, graph):
+        ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev_a.record()
+        if graph is not None:
+            graph.replay()
+        else:
+            for i in range(n):
+                fn(i)
+        ev_b.record()
+        torch.cuda.synchronize()
+        return ev_a.elapsed_time(ev_b) / n
+
     # ---- warmup, then the timed region: exactly `steps` steps --------
+    # (one replay of a graph holding the K steps' launches, so that the
+    # Python binding's per-call cost is not timed; --eager times the calls)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    step_graph = None if args.eager else capture(step, steps)
     t0 = time.perf_counter()
-    ev0.record()
-    for i in range(steps):
-        step(i)
-    ev1.record()
-    torch.cuda.synchronize()
+    ms_per_step = timed(step, steps, step_graph)
     wall = time.perf_counter() - t0
-    ms_per_step = ev0.elapsed_time(ev1) / steps
+    if step_graph is not None:
+        # the replay's outputs (those of the last step) against the same step
+        # issued eagerly, bit for bit
+        gi, gv = idx.clone(), val.clone()
+        step(steps - 1)
+        torch.cuda.synchronize()
+        if not (torch.equal(gi, idx) and torch.equal(gv.view(torch.int32), val.view(torch.int32))):
+            raise RuntimeError("graph replay and eager step disagree")
+        del step_graph
+        ms_per_step_eager = timed(step, steps, None)
+    else:
+        ms_per_step_eager = ms_per_step
 
     # check the timed outputs once (cheap sanity: every row's first index is a
     # visible key or -1)
     first = idx[:, 0].cpu().numpy()
     assert np.all((first >= -1) & (first < n_cols))
 
-    # ---- per-kernel average durations (HIP events, same stream) -------
+    # ---- per-kernel average durations (HIP events, same stream, K launches) --
     def avg_ms(fn):
         for i in range(3):
             fn(i)
         torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(steps):
-            fn(i)
-        b.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(b) / steps
+        g = None if args.eager else capture(fn, steps)
+        ms = timed(fn, steps, g)
+        del g
+        return ms
 
     kernels = {}
     if not args.no_kernel_split:
@@ -388,6 +431,8 @@ def main():
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_eager": ms_per_step_eager,
+        "timing": "eager launches" if args.eager else "one replay of a captured graph of the K steps",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

@@ -99,6 +99,14 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t u) {
     return min(min((uint32_t)__builtin_amdgcn_readlane(v, 0), (uint32_t)__builtin_amdgcn_readlane(v, 16)),
                min((uint32_t)__builtin_amdgcn_readlane(v, 32), (uint32_t)__builtin_amdgcn_readlane(v, 48)));
 }
+// Inclusive prefix sum inside each 16-lane row (shifts by 1, 2, 4 and 8).
+__device__ __forceinline__ int row_incl_scan(int v) {
+    v += dpp_move<0x111>(0, v);  // row_shr:1
+    v += dpp_move<0x112>(0, v);  // row_shr:2
+    v += dpp_move<0x114>(0, v);  // row_shr:4
+    v += dpp_move<0x118>(0, v);  // row_shr:8
+    return v;
+}
 // Inclusive prefix sum over the wave's lanes: shifts by 1, 2, 4 and 8 inside
 // each 16-lane row, then the end of row 0 (and 2) into row 1 (and 3), then
 // the end of row 1 into rows 2 and 3.

@@ -54,6 +54,106 @@ __device__ __forceinline__ unsigned long long lanes_below(int lane) {
     return lane == 0 ? 0ull : (~0ull >> (64 - lane));
 }
 
+// Over one thread's bins of a descending walk (counts c; `run` = position
+// of the first), fills off[] with each bin's start position, finds the bin B
+// holding position total_sel - 1 and returns the largest bin taken whole
+// (ending at or before total_sel).  The one thread holding B stores (bin,
+// keys to take from it, its count) in sc[0..2]; the rest run no branch.
+// Bins past the walk have count 0 and change nothing.
+template <int MAXPER>
+__device__ __forceinline__ int find_boundary_bin(const int (&c)[MAXPER], int run, int total_sel, int nb, int per,
+                                                 int tid, uint32_t (&off)[MAXPER], int *sc) {
+    int fullmax = 0, bq = -1, rb = 0, cb = 0;
+#pragma unroll
+    for (int q = 0; q < MAXPER; ++q) {
+        off[q] = (uint32_t)run;
+        const int end = run + c[q];
+        const bool inb = run < total_sel && end >= total_sel;
+        bq = inb ? q : bq;
+        rb = inb ? run : rb;
+        cb = inb ? c[q] : cb;
+        fullmax = max(fullmax, !inb && end <= total_sel ? c[q] : 0);
+        run = end;
+    }
+    if (bq >= 0) {
+        sc[0] = nb - 1 - (tid * per + bq);
+        sc[1] = total_sel - rb;
+        sc[2] = cb;
+    }
+    return fullmax;
+}
+
+// Combining one value per wave: lane l < NW takes wave l's value from LDS
+// (the identity elsewhere) and DPP moves reduce or scan the first row of 16
+// lanes, a handful of instructions where a loop over the NW words costs a
+// read and an operation per wave, in every wave.
+template <int NW>
+__device__ __forceinline__ int waves_sum(const int *p) {
+    static_assert(NW <= 16, "one row of lanes");
+    const int l = threadIdx.x & 63;
+    const int v = row_reduce(l < NW ? p[l] : 0, 0, [](int a, int b) { return a + b; });
+    return __builtin_amdgcn_readlane(v, 0);
+}
+template <int NW>
+__device__ __forceinline__ uint32_t waves_max_u32(const int *p) {
+    static_assert(NW <= 16, "one row of lanes");
+    const int l = threadIdx.x & 63;
+    const int v = row_reduce(l < NW ? p[l] : 0, 0, [](int a, int b) { return (int)max((uint32_t)a, (uint32_t)b); });
+    return (uint32_t)__builtin_amdgcn_readlane(v, 0);
+}
+template <int NW>
+__device__ __forceinline__ uint32_t waves_min_u32(const int *p) {
+    static_assert(NW <= 16, "one row of lanes");
+    const int l = threadIdx.x & 63;
+    const int v = row_reduce(l < NW ? p[l] : -1, -1, [](int a, int b) { return (int)min((uint32_t)a, (uint32_t)b); });
+    return (uint32_t)__builtin_amdgcn_readlane(v, 0);
+}
+// Exclusive prefix of the NW per-wave values p[0..NW) at this wave, and
+// their total.
+template <int NW>
+__device__ __forceinline__ int waves_excl(const int *p, int &total) {
+    static_assert(NW <= 16, "one row of lanes");
+    const int l = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int s = row_incl_scan(l < NW ? p[l] : 0);
+    total = __builtin_amdgcn_readlane(s, NW - 1);
+    return wid > 0 ? __builtin_amdgcn_readlane(s, wid - 1) : 0;
+}
+
+// A descending walk over nb bins gives thread tid the ranks per*tid ..
+// per*tid + per - 1 (rank r is bin nb - 1 - r; per is 1, 2 or 4).  Those
+// bins are adjacent, so they are read or written with one 8- or 16-byte LDS
+// access: consecutive lanes then touch consecutive words, where per 4-byte
+// accesses 4*per bytes apart would collide on the same banks.
+template <int MAXPER>
+__device__ __forceinline__ void read_bins_desc(const uint32_t *h, int nb, int per, int tid, int (&c)[MAXPER]) {
+#pragma unroll
+    for (int q = 0; q < MAXPER; ++q) c[q] = 0;
+    if (MAXPER >= 4 && per == 4) {
+        const uint4 v = *reinterpret_cast<const uint4 *>(h + nb - 4 * (tid + 1));
+        c[0] = (int)v.w;
+        c[MAXPER > 1 ? 1 : 0] = (int)v.z;
+        c[MAXPER > 2 ? 2 : 0] = (int)v.y;
+        c[MAXPER > 3 ? 3 : 0] = (int)v.x;
+    } else if (MAXPER >= 2 && per == 2) {
+        const uint2 v = *reinterpret_cast<const uint2 *>(h + nb - 2 * (tid + 1));
+        c[0] = (int)v.y;
+        c[MAXPER > 1 ? 1 : 0] = (int)v.x;
+    } else if (tid < nb) {
+        c[0] = (int)h[nb - 1 - tid];
+    }
+}
+template <int MAXPER>
+__device__ __forceinline__ void write_bins_desc(uint32_t *h, int nb, int per, int tid, const uint32_t (&o)[MAXPER]) {
+    if (MAXPER >= 4 && per == 4) {
+        *reinterpret_cast<uint4 *>(h + nb - 4 * (tid + 1)) =
+            make_uint4(o[MAXPER > 3 ? 3 : 0], o[MAXPER > 2 ? 2 : 0], o[MAXPER > 1 ? 1 : 0], o[0]);
+    } else if (MAXPER >= 2 && per == 2) {
+        *reinterpret_cast<uint2 *>(h + nb - 2 * (tid + 1)) = make_uint2(o[MAXPER > 1 ? 1 : 0], o[0]);
+    } else if (tid < nb) {
+        h[nb - 1 - tid] = o[0];
+    }
+}
+
 // Exclusive scan of one int per thread across the workgroup; also returns the
 // total.  `tmp` holds kWaves ints.  Contains two barriers.
 __device__ int block_exclusive_scan(int v, int *tmp, int &total) {
@@ -61,15 +161,8 @@ __device__ int block_exclusive_scan(int v, int *tmp, int &total) {
     const int incl = wave_incl_scan(v);
     if (lane == 63) tmp[wid] = incl;
     __syncthreads();
-    int off = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        const int x = tmp[w];
-        off += w < wid ? x : 0;
-        tot += x;
-    }
+    const int off = waves_excl<kWaves>(tmp, total);
     __syncthreads();
-    total = tot;
     return off + incl - v;
 }
 
@@ -162,15 +255,9 @@ __device__ void topk_row_general(const TopkArgs &a, int k_pad, unsigned char *sm
             tmp[kWaves + wid] = __popcll(me);
         }
         __syncthreads();
-        int og = 0, oe = 0, tg = 0, te = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) {
-            const int xg = tmp[w], xe = tmp[kWaves + w];
-            og += w < wid ? xg : 0;
-            oe += w < wid ? xe : 0;
-            tg += xg;
-            te += xe;
-        }
+        int tg, te;
+        const int og = waves_excl<kWaves>(tmp, tg);
+        const int oe = waves_excl<kWaves>(tmp + kWaves, te);
         const unsigned long long packed = ((unsigned long long)u << 32) | (uint32_t)(~(uint32_t)i);
         if (gt) sel[gt_base + og + __popcll(mg & below)] = packed;
         if (eq) {
@@ -297,34 +384,15 @@ __device__ void scan_bins_desc(const uint32_t *h, uint32_t *start, int nb, int t
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int per = nb > kThreads ? nb / kThreads : 1;
     int c[MAXPER];
+    read_bins_desc<MAXPER>(h, nb, per, tid, c);
     int local = 0;
 #pragma unroll
-    for (int q = 0; q < MAXPER; ++q) {
-        c[q] = 0;
-        const int r = tid * per + q;
-        if (q < per && r < nb) {
-            c[q] = (int)h[nb - 1 - r];
-            local += c[q];
-        }
-    }
+    for (int q = 0; q < MAXPER; ++q) local += c[q];
     int total;
     int run = block_exclusive_scan(local, sc + 64, total);
-    int fullmax = 0;
-#pragma unroll
-    for (int q = 0; q < MAXPER; ++q) {
-        const int r = tid * per + q;
-        if (q < per && r < nb) {
-            if (start) start[nb - 1 - r] = (uint32_t)run;
-            if (run < total_sel && run + c[q] >= total_sel) {
-                sc[0] = nb - 1 - r;
-                sc[1] = total_sel - run;
-                sc[2] = c[q];
-            } else if (run + c[q] <= total_sel) {
-                fullmax = max(fullmax, c[q]);
-            }
-        }
-        run += c[q];
-    }
+    uint32_t off[MAXPER];
+    int fullmax = find_boundary_bin<MAXPER>(c, run, total_sel, nb, per, tid, off, sc);
+    if (start) write_bins_desc<MAXPER>(start, nb, per, tid, off);
     fullmax = (int)wave_max_u32((uint32_t)fullmax);
     if (lane == 0) sc[8 + wid] = fullmax;
     __syncthreads();
@@ -380,15 +448,9 @@ __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int 
     }
     if (tid == 0) sc[3] = 0;
     __syncthreads();
-    int nsel = 0;
-    mn = 0xffffffffu;
-    mx = 0u;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        nsel += sc[8 + w];
-        mn = min(mn, (uint32_t)sc[8 + kWaves + w]);
-        mx = max(mx, (uint32_t)sc[8 + 2 * kWaves + w]);
-    }
+    const int nsel = waves_sum<kWaves>(sc + 8);
+    mn = waves_min_u32<kWaves>(sc + 8 + kWaves);
+    mx = waves_max_u32<kWaves>(sc + 8 + 2 * kWaves);
     const bool all = nsel <= k;
     const int total_sel = all ? nsel : k;
     for (int j = total_sel + tid; j < k; j += kThreads) {
@@ -462,13 +524,8 @@ __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int 
     for (int i = tid; i < 4096; i += kThreads) hist[i] = 0u;
     if (tid == 0) sc[4] = 0;
     __syncthreads();
-    smn = 0xffffffffu;
-    smx = 0u;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        smn = min(smn, (uint32_t)sc[16 + w]);
-        smx = max(smx, (uint32_t)sc[16 + kWaves + w]);
-    }
+    smn = waves_min_u32<kWaves>(sc + 16);
+    smx = waves_max_u32<kWaves>(sc + 16 + kWaves);
     bool sorted_out = false;
     if (smn != smx) {
         const int pos2 = 32 - __clz(smn ^ smx);
@@ -479,9 +536,7 @@ __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int 
             atomicAdd(&hist[(uint32_t)(S[q] >> (32 + shift2)) & (nb2 - 1)], 1u);
         __syncthreads();
         scan_bins_desc(hist, hcur, nb2, total_sel, sc);
-        int bmax = 0;
-#pragma unroll
-        for (int w = 0; w < kWaves; ++w) bmax = max(bmax, sc[8 + w]);
+        const int bmax = (int)waves_max_u32<kWaves>(sc + 8);
         const int B2 = sc[0], need2 = sc[1], cnt2 = sc[2];
         if (bmax <= kMaxBucket && cnt2 <= kLongCand2) {
             const int start2 = total_sel - need2;
@@ -572,15 +627,8 @@ __device__ __forceinline__ int scan_excl(int v, int *tmp, int &total) {
     const int incl = wave_incl_scan(v);
     if (lane == 63) tmp[wid] = incl;
     __syncthreads();
-    int off = 0, tot = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const int x = tmp[w];
-        off += w < wid ? x : 0;
-        tot += x;
-    }
+    const int off = waves_excl<NW>(tmp, total);
     __syncthreads();
-    total = tot;
     return off + incl - v;
 }
 
@@ -605,30 +653,20 @@ __device__ void threshold_bin(const uint32_t *h, int nb, int need, int *sc) {
     constexpr int MAXPER = rows_bins(THREADS) / THREADS;
     const int per = nb > THREADS ? nb / THREADS : 1;  // bins per thread
     int c[MAXPER];
+    read_bins_desc<MAXPER>(h, nb, per, tid, c);
     int local = 0;
 #pragma unroll
-    for (int q = 0; q < MAXPER; ++q) {
-        c[q] = 0;
-        const int r = tid * per + q;
-        if (q < per && r < nb) {
-            c[q] = (int)h[nb - 1 - r];
-            local += c[q];
-        }
-    }
+    for (int q = 0; q < MAXPER; ++q) local += c[q];
     int wsum = local;
     wsum = wave_sum(wsum);
     if (lane == 0) sc[4 + wid] = wsum;
     __syncthreads();
-    // the wave whose bins contain the crossing, and the count before it
-    int before = 0, wstar = NW;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        const int x = sc[4 + w];
-        if (wstar == NW) {
-            if (before + x >= need) wstar = w;
-            else before += x;
-        }
-    }
+    // the wave whose bins contain the crossing (the first whose running
+    // total reaches need), and the count before it
+    const int srun = row_incl_scan(lane < NW ? sc[4 + lane] : 0);
+    const unsigned long long hit = __builtin_amdgcn_ballot_w64(lane < NW && srun >= need);
+    const int wstar = hit ? (int)__builtin_ctzll(hit) : NW;
+    const int before = wstar > 0 && wstar < NW ? __builtin_amdgcn_readlane(srun, wstar - 1) : 0;
     if (wid == wstar) {
         const int incl = wave_incl_scan(local);
         int acc = before + incl - local;
@@ -695,15 +733,9 @@ __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_ker
         sc[8 + 2 * NW + wid] = (int)mx;
     }
     __syncthreads();
-    int nsel = 0;
-    mn = 0xffffffffu;
-    mx = 0u;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) {
-        nsel += sc[8 + w];
-        mn = min(mn, (uint32_t)sc[8 + NW + w]);
-        mx = max(mx, (uint32_t)sc[8 + 2 * NW + w]);
-    }
+    const int nsel = waves_sum<NW>(sc + 8);
+    mn = waves_min_u32<NW>(sc + 8 + NW);
+    mx = waves_max_u32<NW>(sc + 8 + 2 * NW);
 
     int32_t *const idx_out = a.idx + (int64_t)t * a.out_st;
     float *const val_out = a.val ? a.val + (int64_t)t * a.out_st : nullptr;
@@ -739,42 +771,22 @@ __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_ker
             constexpr int MAXPER = NBINS / THREADS;
             const int per = nb > THREADS ? nb / THREADS : 1;
             int c[MAXPER];
+            read_bins_desc<MAXPER>(hist0, nb, per, tid, c);
             int local = 0;
 #pragma unroll
-            for (int q = 0; q < MAXPER; ++q) {
-                c[q] = 0;
-                const int r = tid * per + q;
-                if (q < per && r < nb) {
-                    c[q] = (int)hist0[nb - 1 - r];
-                    local += c[q];
-                }
-            }
+            for (int q = 0; q < MAXPER; ++q) local += c[q];
             int total;
             int run = scan_excl<THREADS>(local, sc + 64, total);
-            int fullmax = 0;  // largest bin taken whole
-#pragma unroll
-            for (int q = 0; q < MAXPER; ++q) {
-                const int r = tid * per + q;
-                if (q < per && r < nb) {
-                    hist1[nb - 1 - r] = (uint32_t)run;  // output offset of the bin
-                    if (run < sel_total && run + c[q] >= sel_total) {
-                        // B: the bin holding the last selected position
-                        sc[0] = nb - 1 - r;
-                        sc[1] = sel_total - run;
-                        sc[2] = c[q];
-                    } else if (run + c[q] <= sel_total) {
-                        fullmax = max(fullmax, c[q]);  // a bin above B, taken whole
-                    }
-                }
-                run += c[q];
-            }
+            // output offsets of the bins, B (the bin holding the last
+            // selected position) and the largest bin above it, taken whole
+            uint32_t off[MAXPER];
+            int fullmax = find_boundary_bin<MAXPER>(c, run, sel_total, nb, per, tid, off, sc);
+            write_bins_desc<MAXPER>(hist1, nb, per, tid, off);
             fullmax = (int)wave_max_u32((uint32_t)fullmax);
             if (lane == 0) sc[8 + wid] = fullmax;
             if (tid == 0) sc[3] = 0;  // keys gathered from bin B
             __syncthreads();
-            int bmax = 0;
-#pragma unroll
-            for (int w = 0; w < NW; ++w) bmax = max(bmax, sc[8 + w]);
+            const int bmax = (int)waves_max_u32<NW>(sc + 8);
             // every thread has read sc[8..]; B and its counts stay in sc[0..2]
             const int B = all0 ? -1 : sc[0];
             const int need_b = all0 ? 0 : sc[1];
@@ -936,30 +948,25 @@ __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_ker
     constexpr int MAXPER = NBINS / THREADS;
     const int per = bnb > THREADS ? bnb / THREADS : 1;
     int c4[MAXPER];
+    read_bins_desc<MAXPER>(bh, bnb, per, tid, c4);
     int local = 0, cmax = 0;
 #pragma unroll
     for (int q = 0; q < MAXPER; ++q) {
-        c4[q] = 0;
-        const int r = tid * per + q;
-        if (q < per && r < bnb) {
-            c4[q] = (int)bh[bnb - 1 - r];
-            local += c4[q];
-            cmax = max(cmax, c4[q]);
-        }
+        local += c4[q];
+        cmax = max(cmax, c4[q]);
     }
     cmax = (int)wave_max_u32((uint32_t)cmax);
     if (lane == 0) sc[8 + wid] = cmax;
     int total;
     int run = scan_excl<THREADS>(local, sc + 64, total);  // its barriers publish sc[8..]
+    uint32_t off4[MAXPER];
 #pragma unroll
     for (int q = 0; q < MAXPER; ++q) {
-        const int r = tid * per + q;
-        if (q < per && r < bnb) bstart[bnb - 1 - r] = (uint32_t)run;
+        off4[q] = (uint32_t)run;
         run += c4[q];
     }
-    int bmax = 0;
-#pragma unroll
-    for (int w = 0; w < NW; ++w) bmax = max(bmax, sc[8 + w]);
+    write_bins_desc<MAXPER>(bstart, bnb, per, tid, off4);
+    const int bmax = (int)waves_max_u32<NW>(sc + 8);
 
     if (bmax <= kMaxBucket && total_sel <= tcap) {
         // scatter into buckets (order inside a bucket arbitrary), then rank

@@ -315,6 +315,59 @@ def test_runs_are_bit_identical():
     assert np.array_equal(a.view(np.uint32), b.view(np.uint32))
 
 
+def test_graph_replays_match_eager():
+    """The fused entry points captured into a HIP graph (as the benchmark
+    times them): every replay, with eager calls on other inputs into the
+    same buffers and synchronisations between replays, gives the eager
+    results bit for bit."""
+    dec = W.random_decode(6, 5, 2, 64, 128, 64, 100, 900, 64)
+    pre = W.random_prefill(8, 40, 700, 64, 128, 32, mask_kind="causal", w_kind="uniform")
+    other = W.random_decode(9, 5, 2, 64, 128, 64, 100, 900, 64)
+    d_in = [dev(x) for x in (dec.q, dec.k_cache, dec.block_table, dec.seq_lens, dec.w)]
+    o_in = [dev(x) for x in (other.q, other.k_cache, other.block_table, other.seq_lens, other.w)]
+    p_in = [dev(x) for x in (pre.q, pre.k, pre.w, pre.mask, pre.vis_len)]
+    R = dec.R * dec.Q
+    d_idx = torch.empty((R, dec.k_top), dtype=torch.int32, device=DEV)
+    d_val = torch.empty((R, dec.k_top), dtype=torch.float32, device=DEV)
+    p_idx = torch.empty((pre.T, pre.k_top), dtype=torch.int32, device=DEV)
+    p_val = torch.empty((pre.T, pre.k_top), dtype=torch.float32, device=DEV)
+    max_sl = max(dec.max_seq_len, other.max_seq_len)
+    d_ws = torch.empty(li.workspace_bytes(li.OP_FUSED_DECODE, R, max_sl, dec.k_top), dtype=torch.uint8, device=DEV)
+    p_ws = torch.empty(li.workspace_bytes(li.OP_FUSED_PREFILL, pre.T, pre.P, pre.k_top), dtype=torch.uint8, device=DEV)
+
+    def run_dec(x, sl_max):
+        q, kc, bt, sl, w = x
+        li.score_topk_fused_decode(q, kc, bt, sl, dec.Q, sl_max, w, dec.k_top, workspace=d_ws, idx=d_idx, val=d_val)
+
+    def run_pre():
+        q, k, w, m, v = p_in
+        li.score_topk_fused_prefill(q, k, w, pre.k_top, m, v, workspace=p_ws, idx=p_idx, val=p_val)
+
+    def both():
+        run_dec(d_in, dec.max_seq_len)
+        run_pre()
+
+    both()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in (d_idx, d_val, p_idx, p_val)]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            both()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        run_dec(o_in, other.max_seq_len)  # eager work on other inputs into the same buffers
+        p_idx.fill_(-7)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip((d_idx, d_val, p_idx, p_val), ref):
+            assert torch.equal(got.view(torch.int32), want.view(torch.int32)), f"replay {rep} differs"
+
+
 def test_heads_major_query_layout():
     """q given as a [H, T, d] tensor viewed as [T, H, d] (strides T*d... ) is
     read through its strides."""
