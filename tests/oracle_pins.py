@@ -66,6 +66,22 @@ def pin_topk_ties(lib):
             assert np.array_equal(np.signbit(val[0]), np.signbit(want))
 
 
+def pin_decode_mask_example(lib):
+    """Masked paged decode worked by hand: the mask row is the query row
+    r*Q + j, finite entries are biases added after the head sum (outside the
+    rectifier), -inf hides a key, and keys past the visible length ignore
+    the mask."""
+    g = load_golden("decode_mask_example.json")
+    q = golden_array(g["q"]).astype(np.float16)
+    kc = golden_array(g["k_cache"]).astype(np.float16)
+    bt = np.array(g["block_table"], dtype=np.int32)
+    sl = np.array(g["seq_lens"], dtype=np.int32)
+    w = golden_array(g["w"]).astype(np.float32)
+    mask = golden_array(g["mask"]).astype(np.float16)
+    got = oracle.score_decode(q, kc, bt, sl, g["Q"], g["max_seq_len"], w, mask, lib=lib)
+    assert np.array_equal(got, golden_array(g["score"])), got
+
+
 def pin_decode_visibility_example(lib):
     g = load_golden("decode_visibility_example.json")
     q = golden_array(g["q"]).astype(np.float16)
@@ -247,14 +263,20 @@ def pin_decode_matches_materialise(lib):
     """Paged decode through a permuted block table vs gathering each
     request's keys and scoring them with the materialised scheme; the cache
     slots no request owns are NaN, so a stray read would show."""
-    for seed, (R, Q, H, d, bs, lo, hi) in enumerate([(3, 1, 4, 16, 8, 5, 40),
-                                                       (2, 4, 8, 32, 16, 3, 50),
-                                                       (4, 3, 64, 128, 64, 1, 130)]):
-        inp = W.random_decode(seed, R, Q, H, d, bs, lo, hi, 8, w_kind="signed")
+    cases = [(3, 1, 4, 16, 8, 5, 40, "none"),
+             (2, 4, 8, 32, 16, 3, 50, "none"),
+             (4, 3, 64, 128, 64, 1, 130, "none"),
+             # masks: finite biases with some -inf, and 0 / -inf; the mask row
+             # of query j of request r is row r*Q + j
+             (3, 2, 4, 16, 8, 5, 40, "bias"),
+             (4, 3, 8, 32, 16, 2, 60, "random"),
+             (3, 4, 64, 128, 64, 4, 100, "bias")]
+    for seed, (R, Q, H, d, bs, lo, hi, mk) in enumerate(cases):
+        inp = W.random_decode(seed, R, Q, H, d, bs, lo, hi, 8, w_kind="signed", mask_kind=mk)
         a = oracle.score_decode(inp.q, inp.k_cache, inp.block_table, inp.seq_lens,
-                                inp.Q, inp.max_seq_len, inp.w, lib=lib)
+                                inp.Q, inp.max_seq_len, inp.w, inp.mask, lib=lib)
         b = materialize.score_decode(inp.q, inp.k_cache, inp.block_table, inp.seq_lens,
-                                     inp.Q, inp.max_seq_len, inp.w)
+                                     inp.Q, inp.max_seq_len, inp.w, inp.mask)
         _close(a, b, rtol=1e-12, atol=1e-12)
 
 

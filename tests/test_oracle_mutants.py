@@ -48,6 +48,10 @@ MUTANTS = [
     ("decode_row_order_swapped", "int64_t t = (int64_t)r * Q + j;", "int64_t t = (int64_t)j * R + r;"),
     ("decode_ignores_block_table", "(phys * block_size + s % block_size)", "((int64_t)s)"),
     ("decode_first_block_only", "s / block_size];", "0];"),
+    ("decode_mask_dropped", "                if (mask)\n                    v += half_to_double(mask[t * mask_stride_t + s]);", ""),
+    ("decode_mask_row_by_request", "mask[t * mask_stride_t + s]", "mask[(int64_t)r * mask_stride_t + s]"),
+    ("decode_mask_inside_relu", "v += half_to_double(mask[t * mask_stride_t + s]);",
+     "v = fmax(v + half_to_double(mask[t * mask_stride_t + s]), 0.0);"),
 ]
 
 
