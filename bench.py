@@ -3,17 +3,17 @@
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config NAME]
 
-One step is the whole hot path over one batch of synthetic input.  Paged
-keys (decode, spec_decode) go through the fused entry point (the score
-kernel into a workspace, then the per-row top-k kernel); contiguous keys run
-the score into a [rows, keys] f32 buffer, then the per-row top-k.  The timed region is exactly K steps
-between two synchronisations: by default one replay of a HIP graph captured
-from the K steps' calls (so the Python binding's per-call cost is not
-timed; the replay's last outputs are checked bit for bit against the same
-step issued eagerly, and the eager rate is reported beside it), with
---eager the K calls themselves.  Inputs are resident in HBM before it
-starts, and several copies of them are rotated so that consecutive steps do
-not hit the 256 MB Infinity Cache.
+One step is the whole hot path over one batch of synthetic input: the fused
+score + top-k entry point of the workload's kind.  The timed region is
+exactly K steps between two synchronisations: by default the replays of HIP
+graphs captured from the K steps' calls, split into (at most) ten batches of
+consecutive steps with an event between batches (so the Python binding's
+per-call cost is not timed; the last outputs are checked bit for bit against
+the same step issued eagerly, and the eager rate is reported beside it), with
+--eager the K calls themselves.  ``ms_per_step`` is the whole region over K;
+``ms_per_step_median`` the median over the batches.  Inputs are resident in
+HBM before it starts, and several copies of them are rotated so that
+consecutive steps do not hit the 256 MB Infinity Cache.
 
 Prints ONE JSON line: throughput in visible (token, key) pairs per second,
 the roofline of the dominant kernel (its average duration measured with HIP
@@ -23,10 +23,11 @@ oracle timed on a bounded sample of the same workload as a baseline.
 
 Workloads (``--config``):
   tiny            16 tokens x 256 keys, 4 heads of 64, top-32
-  decode          32 requests x 1 query, 1024..8192 paged keys, 64 heads of 128, top-512 (default)
+  decode          32 requests x 1 query, 1024..8192 paged keys, 64 heads of 128, top-512
   spec_decode     32 requests x 4 queries, 16384 paged keys, top-2048
   prefill_causal  8192 tokens x 8192 keys, causal f16 mask, top-2048
-  long_chunk      1024-token chunk x 131072 keys, causal, top-2048
+  long_chunk      1024-token chunk x 131072 keys, causal, top-2048 (default: the
+                  largest workload, 2.19 TFLOP of visible pairs per step)
 """
 from __future__ import annotations
 
@@ -166,7 +167,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
-    ap.add_argument("--config", default="decode",
+    ap.add_argument("--config", default="long_chunk",
                     choices=["tiny", "decode", "spec_decode", "prefill_causal", "long_chunk"])
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
@@ -311,17 +312,17 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # A HIP graph of n launches of fn(i), captured on a side stream (the
-    # library launches on torch's current stream, which capture redirects);
-    # the library allocates nothing and records no memset, so replays
-    # repeat the same kernels on the same buffers.
-    def capture(fn, n):
+    # HIP graphs of consecutive launches fn(lo) .. fn(hi-1), captured on a
+    # side stream (the library launches on torch's current stream, which
+    # capture redirects); the library allocates nothing and records no
+    # memset, so replays repeat the same kernels on the same buffers.
+    def capture(fn, lo, hi):
         s = torch.cuda.Stream()
         s.wait_stream(torch.cuda.current_stream())
         g = torch.cuda.CUDAGraph()
         with torch.cuda.stream(s):
             with torch.cuda.graph(g, stream=s):
-                for i in range(n):
+                for i in range(lo, hi):
                     fn(i)
         torch.cuda.current_stream().wait_stream(s)
         torch.cuda.synchronize()
@@ -329,29 +330,43 @@ def main():
         torch.cuda.synchronize()
         return g
 
-    def timed(fn, n, graph):
-        ev_a, ev_b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev_a.record()
-        if graph is not None:
-            graph.replay()
-        else:
-            for i in range(n):
-                fn(i)
-        ev_b.record()
+    def batches(n):
+        nb = min(10, n)
+        edges = [round(i * n / nb) for i in range(nb + 1)]
+        return [(edges[i], edges[i + 1]) for i in range(nb)]
+
+    def timed(fn, n, graphs):
+        """Exactly n launches fn(0) .. fn(n-1) in batches, an event between
+        batches, one synchronisation at the end.  Returns (whole region / n,
+        median over batches of the batch time per launch)."""
+        parts = batches(n)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(len(parts) + 1)]
+        evs[0].record()
+        for b, (lo, hi) in enumerate(parts):
+            if graphs is not None:
+                graphs[b].replay()
+            else:
+                for i in range(lo, hi):
+                    fn(i)
+            evs[b + 1].record()
         torch.cuda.synchronize()
-        return ev_a.elapsed_time(ev_b) / n
+        per = [evs[b].elapsed_time(evs[b + 1]) / (hi - lo) for b, (lo, hi) in enumerate(parts)]
+        return evs[0].elapsed_time(evs[-1]) / n, float(np.median(per))
+
+    def graphs_for(fn, n):
+        return None if args.eager else [capture(fn, lo, hi) for lo, hi in batches(n)]
 
     # ---- warmup, then the timed region: exactly `steps` steps --------
-    # (one replay of a graph holding the K steps' launches, so that the
-    # Python binding's per-call cost is not timed; --eager times the calls)
+    # (replays of graphs holding the K steps' launches, so that the Python
+    # binding's per-call cost is not timed; --eager times the calls)
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    step_graph = None if args.eager else capture(step, steps)
+    step_graphs = graphs_for(step, steps)
     t0 = time.perf_counter()
-    ms_per_step = timed(step, steps, step_graph)
+    ms_per_step, ms_per_step_median = timed(step, steps, step_graphs)
     wall = time.perf_counter() - t0
-    if step_graph is not None:
+    if step_graphs is not None:
         # the replay's outputs (those of the last step) against the same step
         # issued eagerly, bit for bit
         gi, gv = idx.clone(), val.clone()
@@ -359,8 +374,8 @@ def main():
         torch.cuda.synchronize()
         if not (torch.equal(gi, idx) and torch.equal(gv.view(torch.int32), val.view(torch.int32))):
             raise RuntimeError("graph replay and eager step disagree")
-        del step_graph
-        ms_per_step_eager = timed(step, steps, None)
+        del step_graphs
+        ms_per_step_eager, _ = timed(step, steps, None)
     else:
         ms_per_step_eager = ms_per_step
 
@@ -374,15 +389,15 @@ def main():
         for i in range(3):
             fn(i)
         torch.cuda.synchronize()
-        g = None if args.eager else capture(fn, steps)
+        g = graphs_for(fn, steps)
         ms = timed(fn, steps, g)
         del g
         return ms
 
-    kernels = {}
+    kernels, kernels_median = {}, {}
     if not args.no_kernel_split:
-        kernels["score"] = avg_ms(lambda i: run_score(copies[i % n_copies]))
-        kernels["topk"] = avg_ms(lambda i: run_topk())
+        kernels["score"], kernels_median["score"] = avg_ms(lambda i: run_score(copies[i % n_copies]))
+        kernels["topk"], kernels_median["topk"] = avg_ms(lambda i: run_topk())
 
     # ---- roofline of the dominant kernel --------------------------------
     out_bytes = n_rows * k_top * 8
@@ -416,7 +431,8 @@ def main():
         if not args.no_peak_probe:
             # the same kernel against what this device sustains: an LDS-fed
             # f16 MFMA stream, or a 4 GiB streaming read
-            peaks = li.probe_peaks(dev)
+            from sparse_attention_lightning_indexer_amd.peak_probe import probe_peaks
+            peaks = probe_peaks(dev)
             measured = peaks["read_gbs"] if roof["bound"] == "hbm" else peaks["mfma_f16_tflops"]
             roof["measured_peak"] = measured
             roof["frac_of_measured"] = roof["achieved"] / measured
@@ -431,8 +447,10 @@ def main():
         "steps": steps,
         "warmup": warmup,
         "ms_per_step": ms_per_step,
+        "ms_per_step_median": ms_per_step_median,
         "ms_per_step_eager": ms_per_step_eager,
-        "timing": "eager launches" if args.eager else "one replay of a captured graph of the K steps",
+        "timing": ("eager launches" if args.eager else "replays of captured graphs of the K steps") +
+                  f", {min(10, steps)} batches; ms_per_step = region / K, median over batches beside it",
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -443,6 +461,7 @@ def main():
                    "input_copies": n_copies},
         "roofline": roof,
         "kernels_ms": kernels,
+        "kernels_ms_median": kernels_median,
         "wall_s": wall,
     }
     if not args.no_cpu_baseline:
@@ -454,10 +473,23 @@ def main():
             f.write(text + "\n")
 
 
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(inp, vis_rows, seconds):
     """The CPU oracle (fp64, OpenMP over the host cores) on a bounded sample
-    of the same workload: score + top-k for a subset of rows, repeated until
-    about `seconds` of wall time; reported as visible pairs per second."""
+    of the same workload: score and top-k of a subset of rows, each timed on
+    its own and repeated until about `seconds` of wall time in all; reported
+    as visible pairs per second of score + top-k, and of each alone."""
     import oracle
     n_rows = len(vis_rows)
     # rows per repetition: keep one repetition around a second on a few cores
@@ -475,18 +507,26 @@ def cpu_baseline(inp, vis_rows, seconds):
         rows = [r * inp.Q + j for r in reqs for j in range(inp.Q)]
     rows = np.array(sorted(set(rows)))
     sample_pairs = int(vis_rows[rows].sum())
-    reps, t0 = 0, time.perf_counter()
+    reps, t_score, t_topk = 0, 0.0, 0.0
     while True:
+        t0 = time.perf_counter()
         s = oracle.score_rows(inp, rows)
+        t1 = time.perf_counter()
         oracle.topk(s, inp.k_top)
+        t2 = time.perf_counter()
+        t_score += t1 - t0
+        t_topk += t2 - t1
         reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or reps >= 1000:
+        if t_score + t_topk >= seconds or reps >= 1000:
             break
+    el = t_score + t_topk
     return {"value": sample_pairs * reps / el, "unit": "pairs/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model(),
+            "score_pairs_per_s": sample_pairs * reps / t_score,
+            "topk_pairs_per_s": sample_pairs * reps / t_topk,
             "sample": f"{len(rows)} of {n_rows} score rows ({sample_pairs} visible pairs), "
-                      f"score + top-{inp.k_top}, repeated {reps}x in {el:.1f} s"}
+                      f"score then top-{inp.k_top} (timed apart: {t_score:.1f} s and {t_topk:.1f} s), "
+                      f"repeated {reps}x"}
 
 
 if __name__ == "__main__":

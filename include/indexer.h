@@ -220,28 +220,6 @@ indexer_status indexer_score_topk_fused_decode(
  */
 size_t indexer_workspace_bytes(int op, int32_t n_rows, int32_t n_cols, int32_t k_top);
 
-/*
- * Measurement helpers (not part of the indexer): what the device sustains for
- * the two bounds the kernels are measured against, to report a fraction of
- * the measured peak beside the fraction of the published one.  Both launch
- * asynchronously on `stream`; the caller times them (events on that stream).
- *
- * indexer_probe_mfma -- 2 workgroups of 256 threads per compute unit, each
- *   wave running iters x 128 v_mfma_f32_32x32x16_f16 fed as the score
- *   kernels feed them (B fragments from swizzled LDS rows, four accumulators
- *   per fragment, two fragments in flight), on pseudo-random f16 operands
- *   (the rate depends on the operand bits).  *flops receives the f16 flops of
- *   the launch.  sink: device buffer of indexer_probe_sink_floats() floats
- *   (written only in a case that never occurs).  EINVAL for iters < 1 or a
- *   NULL pointer.
- * indexer_probe_read -- one streaming read of `bytes` (a positive multiple of
- *   16) at `buf` (device, 16-byte aligned), 16 bytes per lane per load.
- *   sink as above.  EINVAL for a bad pointer, alignment or size.
- */
-int32_t indexer_probe_sink_floats(void);
-indexer_status indexer_probe_mfma(int32_t iters, float *sink, double *flops, void *stream);
-indexer_status indexer_probe_read(const void *buf, size_t bytes, float *sink, void *stream);
-
 #ifdef __cplusplus
 }
 #endif

@@ -2,7 +2,10 @@
 
 Run as ``python -m sparse_attention_lightning_indexer_amd.build``.  Each
 source is compiled to an object under ``_build/`` (in parallel), then linked
-into ``sparse_attention_lightning_indexer_amd/libindexer.so``.
+into ``sparse_attention_lightning_indexer_amd/libindexer.so`` (the indexer's
+C-ABI).  The measured-peak probes the benchmark reports beside the published
+peaks are linked into a separate ``libpeak_probe.so``, outside the indexer's
+ABI.
 """
 from __future__ import annotations
 
@@ -16,7 +19,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libindexer.so")
-SOURCES = ["indexer_api.hip", "score_kernel.hip", "decode_kernel.hip", "topk_kernel.hip", "peak_probe.hip"]
+SOURCES = ["indexer_api.hip", "score_kernel.hip", "decode_kernel.hip", "topk_kernel.hip"]
+PROBE_SOURCES = ["peak_probe.hip"]
+PROBE_LIB = os.path.join(PKG, "libpeak_probe.so")
 ARCH = os.environ.get("INDEXER_OFFLOAD_ARCH", "gfx950")
 
 FLAGS = [
@@ -43,18 +48,24 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(_compile, SOURCES))
-    tmp = LIB + ".tmp"
+def _link(objs, out):
+    tmp = out + ".tmp"
     cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
+
+
+def build(verbose: bool = False) -> str:
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(_compile, srcs))
+    _link(objs[: len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PROBE_LIB}")
     return LIB
 
 

@@ -263,21 +263,6 @@ const char *indexer_status_string(int status) {
 
 const char *indexer_last_error(void) { return g_last_error; }
 
-int32_t indexer_probe_sink_floats(void) { return lidx::probe_sink_floats(); }
-
-indexer_status indexer_probe_mfma(int32_t iters, float *sink, double *flops, void *stream) {
-    if (iters < 1) return fail(INDEXER_EINVAL, "iters=%d must be >= 1", iters);
-    if (!sink || !flops) return fail(INDEXER_EINVAL, "sink and flops must not be NULL");
-    return hip_status(lidx::launch_probe_mfma(iters, sink, flops, (hipStream_t)stream), "probe launch");
-}
-
-indexer_status indexer_probe_read(const void *buf, size_t bytes, float *sink, void *stream) {
-    if (!buf || !sink) return fail(INDEXER_EINVAL, "buf and sink must not be NULL");
-    if (!aligned(buf, 16) || bytes % 16 || bytes == 0)
-        return fail(INDEXER_EINVAL, "buf must be 16-byte aligned and bytes a positive multiple of 16");
-    return hip_status(lidx::launch_probe_read(buf, bytes, sink, (hipStream_t)stream), "probe launch");
-}
-
 size_t indexer_workspace_bytes(int op, int32_t n_rows, int32_t n_cols, int32_t k_top) {
     if (n_rows < 0 || n_cols < 0 || k_top < 0) return (size_t)-1;
     switch (op) {

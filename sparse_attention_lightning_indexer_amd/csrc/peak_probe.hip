@@ -1,6 +1,23 @@
 // Achievable-peak probes for gfx950: what the chip sustains for the two
 // bounds the indexer kernels are measured against, next to the published
 // peaks.  Measurement helpers only; nothing of the indexer's arithmetic.
+// Built into its own library, libpeak_probe.so, which only the benchmark and
+// its test load; the indexer library does not contain or export it.
+//
+// C-ABI (all launches asynchronous on `stream`, a hipStream_t; the caller
+// times them with events on that stream):
+//   int32_t peak_probe_sink_floats(void)
+//       floats of the `sink` device buffer both probes take (written only in
+//       a case that never occurs).
+//   int peak_probe_mfma(int32_t iters, float *sink, double *flops, void *stream)
+//       2 workgroups of 256 threads per compute unit, each wave running
+//       iters x 128 v_mfma_f32_32x32x16_f16; *flops receives the f16 flops
+//       of the launch.  Returns 1 for iters < 1 or a NULL pointer, 4 when the
+//       launch fails, else 0.
+//   int peak_probe_read(const void *buf, size_t bytes, float *sink, void *stream)
+//       one streaming read of `bytes` (a positive multiple of 16) at `buf`
+//       (device, 16-byte aligned).  Returns 1 for a bad pointer, alignment or
+//       size, 4 when the launch fails, else 0.
 //
 //  * probe_mfma_kernel: v_mfma_f32_32x32x16_f16 fed the way the score
 //    kernels feed it -- A fragments in registers, one 16-byte B fragment per
@@ -14,7 +31,6 @@
 //    eight workgroups of 256 threads per compute unit.
 // Both keep their results live through a store that never happens.
 #include "device_common.h"
-#include "internal.h"
 
 namespace lidx {
 namespace {
@@ -96,21 +112,34 @@ __global__ void __launch_bounds__(256) probe_read_kernel(const float4 *p, size_t
     if (acc.x + acc.y + acc.z + acc.w == 1.2345e-30f) sink[blockIdx.x] = acc.x;
 }
 
+int cu_count() {
+    int dev = 0, v = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 256;
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || v <= 0) return 256;
+    return v;
+}
+
 }  // namespace
-
-hipError_t launch_probe_mfma(int iters, float *sink, double *flops, hipStream_t stream) {
-    const int grid = 2 * device_cu_count();
-    hipLaunchKernelGGL(probe_mfma_kernel, dim3(grid), dim3(256), 0, stream, iters, sink);
-    *flops = (double)grid * 4 /*waves*/ * iters * kProbeBlocks * 8 * kProbeMB * (32.0 * 32 * 16 * 2);
-    return hipGetLastError();
-}
-
-hipError_t launch_probe_read(const void *buf, size_t bytes, float *sink, hipStream_t stream) {
-    const int grid = 8 * device_cu_count();
-    hipLaunchKernelGGL(probe_read_kernel, dim3(grid), dim3(256), 0, stream, (const float4 *)buf, bytes / 16, sink);
-    return hipGetLastError();
-}
-
-int probe_sink_floats() { return 8 * device_cu_count(); }
-
 }  // namespace lidx
+
+extern "C" {
+
+int32_t peak_probe_sink_floats(void) { return 8 * lidx::cu_count(); }
+
+int peak_probe_mfma(int32_t iters, float *sink, double *flops, void *stream) {
+    if (iters < 1 || !sink || !flops) return 1;
+    const int grid = 2 * lidx::cu_count();
+    hipLaunchKernelGGL(lidx::probe_mfma_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream, iters, sink);
+    *flops = (double)grid * 4 /*waves*/ * iters * lidx::kProbeBlocks * 8 * lidx::kProbeMB * (32.0 * 32 * 16 * 2);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int peak_probe_read(const void *buf, size_t bytes, float *sink, void *stream) {
+    if (!buf || !sink || ((uintptr_t)buf % 16) || bytes % 16 || bytes == 0) return 1;
+    const int grid = 8 * lidx::cu_count();
+    hipLaunchKernelGGL(lidx::probe_read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
+                       (const float4 *)buf, bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+}  // extern "C"

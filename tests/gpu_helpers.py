@@ -78,24 +78,41 @@ def _oracle_rows(inp, rows):
     return np.where(np.isneginf(s), 0.0, s)      # columns past a row's visible keys
 
 
-def denominators(inp, rows=None):
-    """sum_h |w_h| relu(dot_h) + |mask| + ABS_FLOOR * sum_h |w_h| sum_i |q_hi k_i|
-    for every entry of the given rows (the score bar of this module)."""
+def denominator_parts(inp, rows=None):
+    """(main, floor) for every entry of the given rows: main is
+    sum_h |w_h| relu(dot_h) + |mask| (the plain relative-error denominator when
+    w >= 0 and the mask is 0), floor is ABS_FLOOR * sum_h |w_h| sum_i |q_hi k_i|."""
     ia = dataclasses.replace(abs_weights(inp), mask=None)
     if hasattr(ia, "vis_len"):
         ia = dataclasses.replace(ia, vis_len=None)
-    s = _oracle_rows(ia, rows)
+    main = _oracle_rows(ia, rows)
     # with |q| and |k| every dot product is the sum of the absolute products
     if hasattr(ia, "k_cache"):
         ib = dataclasses.replace(ia, q=np.abs(ia.q), k_cache=np.abs(ia.k_cache))
     else:
         ib = dataclasses.replace(ia, q=np.abs(ia.q), k=np.abs(ia.k))
-    s = s + ABS_FLOOR * _oracle_rows(ib, rows)
+    floor = ABS_FLOOR * _oracle_rows(ib, rows)
     if inp.mask is not None:
         m = inp.mask if rows is None else inp.mask[np.asarray(rows)]
         m = m.astype(np.float64)
-        s = s + np.where(np.isneginf(m), 0.0, np.abs(m))
-    return s
+        main = main + np.where(np.isneginf(m), 0.0, np.abs(m))
+    return main, floor
+
+
+class Den(np.ndarray):
+    """The score bar's denominator (main + floor), carrying the floor-free
+    part so that check_scores can report the error without the floor."""
+
+
+def denominators(inp, rows=None):
+    main, floor = denominator_parts(inp, rows)
+    den = (main + floor).view(Den)
+    den.main = main
+    return den
+
+
+# per-workload summary of the unfloored error, printed by the tests (-s)
+UNFLOORED = {}
 
 
 def check_scores(g, o, den, tol=TOL, where=""):
@@ -106,10 +123,20 @@ def check_scores(g, o, den, tol=TOL, where=""):
     assert bad.size == 0, f"{where}: -inf sets differ at {bad[:5].tolist()} (gpu {g[tuple(bad[0])]}, oracle {o[tuple(bad[0])]})"
     vis = ~inv_o
     assert np.all(np.isfinite(g[vis])), f"{where}: non-finite visible GPU score"
-    err = np.abs(g[vis] - o[vis]) / (den[vis] + 1e-30)
+    diff = np.abs(g[vis] - o[vis])
+    err = diff / (np.asarray(den)[vis] + 1e-30)
     if err.size:
         i = int(np.argmax(err))
         assert err[i] <= tol, f"{where}: max scaled error {err[i]:.3e} (gpu {g[vis][i]}, oracle {o[vis][i]})"
+    main = getattr(den, "main", None)
+    if main is not None and err.size:
+        # the same error without the cancellation floor: plain relative error
+        # (w >= 0, mask 0) or its signed-weight form
+        raw = diff / (main[vis] + 1e-30)
+        needed = int(np.count_nonzero(raw > tol))
+        UNFLOORED[where] = (float(raw.max()), needed, int(raw.size))
+        print(f"{where}: max error {err.max():.2e} with the floor, {raw.max():.2e} without it; "
+              f"{needed} of {raw.size} entries need the floor")
     return float(err.max()) if err.size else 0.0
 
 

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12, names  # 9 for the indexer, 3 measurement helpers
+    assert len(names) == 9, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(li.EXPORTS)
@@ -155,12 +155,16 @@ def test_fused_workspace_checks(lib):
     assert st == li.EWORKSPACE
 
 
-def test_probe_argument_checks(lib):
-    """The measured-peak probes validate before launching (no GPU needed)."""
+def test_probe_argument_checks():
+    """The measured-peak probes (their own library, not the indexer's ABI)
+    validate before launching (no GPU needed)."""
+    from sparse_attention_lightning_indexer_amd import peak_probe
+    pl = peak_probe.load_library()
     d = ctypes.c_double(0.0)
-    assert lib.indexer_probe_mfma(0, A, ctypes.byref(d), None) == li.EINVAL
-    assert lib.indexer_probe_mfma(10, None, ctypes.byref(d), None) == li.EINVAL
-    assert lib.indexer_probe_read(None, 1 << 20, A, None) == li.EINVAL
-    assert lib.indexer_probe_read(A + 4, 1 << 20, A, None) == li.EINVAL
-    assert lib.indexer_probe_read(A, 17, A, None) == li.EINVAL
-    assert b"multiple of 16" in lib.indexer_last_error()
+    assert pl.peak_probe_mfma(0, A, ctypes.byref(d), None) == 1
+    assert pl.peak_probe_mfma(10, None, ctypes.byref(d), None) == 1
+    assert pl.peak_probe_read(None, 1 << 20, A, None) == 1
+    assert pl.peak_probe_read(A + 4, 1 << 20, A, None) == 1
+    assert pl.peak_probe_read(A, 17, A, None) == 1
+    lib = li.load_library()
+    assert not any(hasattr(lib, n) for n in ("indexer_probe_mfma", "indexer_probe_read"))

@@ -112,20 +112,20 @@ def test_random_decode(R, Q, H, d, bs, lo, hi, k_top):
 
 
 # Larger cases for the persistent decode kernel: each workgroup gets many
-# key tiles spanning several row groups (and, with one query row, more tiles
-# than its score staging area holds); the last two shapes take the chunked
-# kernel instead (block size below 4, more than 2048 row groups).
+# key tiles spanning several row groups; the last two shapes take the chunked
+# kernel instead (block size below 4, more than 1536 row groups).
 STREAM_CASES = [
     # R, Q, H, d, block_size, len_lo, len_hi, k_top
     (700, 1, 64, 128, 64, 1, 1500, 64),      # many short requests per workgroup
-    (48, 1, 64, 128, 64, 9000, 14000, 128),  # > 16 tiles per workgroup: staging flushes
+    (48, 1, 64, 128, 64, 9000, 14000, 128),  # > 16 tiles per workgroup
     (300, 4, 64, 128, 16, 4, 1200, 32),      # general mapping: q reloaded per row group
     (200, 2, 32, 64, 37, 1, 3000, 40),       # block size not a power of two
     (100, 3, 8, 128, 4, 1, 2000, 20),        # smallest block size of the persistent kernel
-    (40, 16, 4, 64, 16, 100, 3000, 24),      # 16 rows per group: a flush every 2 tiles
+    (40, 16, 4, 64, 16, 100, 3000, 24),      # 16 rows per group, several row groups per tile stream
     (60, 9, 64, 128, 64, 9, 2500, 16),       # two row groups per request
+    (1500, 1, 64, 128, 64, 1, 400, 16),      # 1500 row groups: near the persistent kernel's 1536
     (50, 1, 16, 64, 2, 1, 800, 10),          # block size 2: chunked kernel
-    (2100, 1, 4, 64, 16, 1, 200, 8),         # 2100 row groups: per-group words fill much of the LDS
+    (2100, 1, 4, 64, 16, 1, 200, 8),         # 2100 row groups: chunked kernel
 ]
 
 
@@ -243,8 +243,60 @@ def test_zero_rows_are_a_no_op():
 
 
 def test_decode_with_mask_and_signed_weights():
-    inp = W.random_decode(42, 4, 4, 64, 128, 64, 50, 400, 32, w_kind="signed", mask_kind="bias")
+    """Row width 321 (not a multiple of 8): the chunked kernel's mask path."""
+    inp = W.random_decode(42, 4, 4, 64, 128, 64, 50, 400, 32, w_kind="signed", mask_kind="bias",
+                          max_seq_len=321)
     _full_check(inp, inp.name)
+
+
+# Masked calls the persistent kernel takes (row width a multiple of 8, block
+# size >= 4): the mask travels with the key tiles through its LDS ring.
+MASKED_STREAM_CASES = [
+    # R, Q, H, d, block_size, len_lo, len_hi, max_seq_len, k_top, mask
+    (40, 1, 64, 128, 64, 1, 3000, 3008, 64, "bias"),     # split mapping, one query row
+    (200, 1, 64, 128, 64, 1, 1000, 1024, 32, "random"),  # split mapping, many row groups per CU
+    (32, 4, 64, 128, 64, 4, 5000, 5000, 128, "bias"),    # spec-decode shape, four rows a group
+    (24, 4, 64, 128, 16, 4, 2000, 2048, 40, "random"),   # block size 16
+    (30, 16, 16, 64, 16, 16, 1500, 1504, 24, "bias"),    # general mapping, two row groups per request
+    (50, 3, 8, 128, 4, 3, 900, 904, 20, "random"),       # general mapping, block size 4
+    (20, 9, 64, 128, 64, 9, 2500, 2504, 16, "bias"),     # split mapping, three row groups per request
+    (60, 2, 4, 64, 37, 2, 700, 704, 12, "random"),       # 4 heads, block size not a power of two
+]
+
+
+@pytest.mark.parametrize("R,Q,H,d,bs,lo,hi,width,k_top,mk", MASKED_STREAM_CASES,
+                         ids=[f"R{c[0]}Q{c[1]}H{c[2]}d{c[3]}bs{c[4]}L{c[5]}-{c[6]}w{c[7]}-{c[9]}"
+                              for c in MASKED_STREAM_CASES])
+def test_masked_stream_decode(R, Q, H, d, bs, lo, hi, width, k_top, mk):
+    inp = W.random_decode(1300 + R + Q + H + bs, R, Q, H, d, bs, lo, hi, k_top, w_kind="signed",
+                          max_seq_len=width, mask_kind=mk)
+    _full_check(inp, inp.name)
+    # masked keys are never selected
+    gi, _ = gpu_fused(inp)
+    picked = np.take_along_axis(inp.mask, np.where(gi >= 0, gi, 0), axis=1).astype(np.float32)
+    assert not np.any(np.isneginf(picked) & (gi >= 0))
+
+
+@pytest.mark.parametrize("permute", [True, False], ids=["permuted", "identity"])
+@pytest.mark.parametrize("H,d,bs", [(64, 128, 64), (16, 64, 16), (4, 128, 8)])
+def test_integer_inputs_paged_bit_exact(H, d, bs, permute):
+    """Exact-arithmetic inputs through the paged path: the same keys laid out
+    in blocks through a permuted or an in-order block table, query j of the
+    T rows seeing the first P - T + 1 + j keys.  Every partial sum is
+    representable in f32, so the GPU equals the oracle bit for bit, and its
+    top-k equals the oracle's top-k of the exact scores."""
+    base = W.integer_prefill(88 + H + d + bs, 13, 777, H, d, 40, mask_kind="none")
+    paged = W.paged_from_prefill(base, bs, permute=permute)
+    g_t = gpu_score(paged)
+    g = g_t.cpu().numpy()
+    o = oracle.score_inputs(paged)
+    assert np.array_equal(g.astype(np.float64), o)
+    gi, gv = gpu_topk(g_t, paged.k_top)
+    oi, ov = oracle.topk(o, paged.k_top)
+    assert np.array_equal(gi, oi)
+    assert np.array_equal(gv.astype(np.float64), ov)
+    fi, fv = gpu_fused(paged)
+    assert np.array_equal(fi, oi)
 
 
 def test_decode_wider_rows_than_lengths():
@@ -475,14 +527,19 @@ def test_workload_decode():
 
 
 def test_workload_spec_decode():
+    """Every one of the 128 rows against the oracle."""
     inp = W.spec_decode()
-    rows = np.array([0, 1, 2, 3, 37, 38, 64, 127])
+    rows = np.arange(inp.R * inp.Q)
     _sampled_check(inp, rows, "spec_decode")
 
 
 def test_workload_prefill_causal():
+    """64 rows in contiguous stripes: every row slot of the kernel's row
+    groups (8 rows each), the first rows (one key chunk), rows around the
+    k_top = 2048 visible-key boundary, and the last rows (every key chunk)."""
     inp = W.prefill_causal()
-    rows = np.array([0, 1, 7, 8, 100, 2046, 2047, 2048, 4095, 5000, 8190, 8191])
+    rows = np.concatenate([np.arange(0, 16), np.arange(2040, 2056), np.arange(5000, 5016),
+                           np.arange(8176, 8192)])
     g = _sampled_check(inp, rows, "prefill_causal")
     # causal: row t has exactly t+1 finite entries
     finite = np.isfinite(g).sum(axis=1)
@@ -490,14 +547,18 @@ def test_workload_prefill_causal():
 
 
 def test_workload_long_chunk():
+    """64 rows in contiguous stripes at the start, middle and end of the
+    chunk (every row slot of the kernel's row groups; every row spans every
+    key chunk)."""
     inp = W.long_chunk()
-    rows = np.array([0, 1, 511, 1022, 1023])
+    rows = np.concatenate([np.arange(0, 24), np.arange(504, 520), np.arange(1000, 1024)])
     _sampled_check(inp, rows, "long_chunk")
 
 
 def test_peak_probes_measure_something():
     """The measured-peak probes run and report plausible rates (well above a
     tenth and below twice the published 2.5 PFLOP/s and 8 TB/s)."""
-    r = li.probe_peaks(DEV, mfma_iters=200, read_bytes=256 << 20, repeats=1)
+    from sparse_attention_lightning_indexer_amd.peak_probe import probe_peaks
+    r = probe_peaks(DEV, mfma_iters=200, read_bytes=256 << 20, repeats=1)
     assert 250.0 < r["mfma_f16_tflops"] < 5000.0, r
     assert 800.0 < r["read_gbs"] < 16000.0, r
