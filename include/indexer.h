@@ -213,6 +213,38 @@ indexer_status indexer_score_topk_fused_decode(
     void *stream);
 
 /*
+ * indexer_score_topk_fused_decode_noalloc -- for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): indexer_score_topk_fused_decode with the
+ * score rows kept in a static device array of INDEXER_NOALLOC_SCRATCH_BYTES
+ * inside the library (one per GPU, held until the process ends) instead of a
+ * caller workspace.  The call allocates and frees nothing.  Arguments,
+ * results and errors as in indexer_score_topk_fused_decode, except that
+ * INDEXER_EWORKSPACE is returned (before anything is enqueued) when the rows
+ * need more than that:
+ *   indexer_workspace_bytes(INDEXER_OP_FUSED_DECODE, n_requests*query_len,
+ *                           max_seq_len, k_top) > INDEXER_NOALLOC_SCRATCH_BYTES
+ * (16 MiB: for example 128 rows of 16384 keys, or 512 rows of 8192).  Every
+ * call on one GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, or different host threads without ordering) race and
+ * give undefined results; calls ordered on one stream are safe.  The first
+ * call on a device looks up the array's address there (hipGetSymbolAddress,
+ * with that device current).
+ */
+#define INDEXER_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+indexer_status indexer_score_topk_fused_decode_noalloc(
+    const void *q, int64_t q_stride_t, int64_t q_stride_h,
+    const void *k_cache, int32_t block_size, int64_t k_stride_s,
+    const int32_t *block_table, int64_t bt_stride,
+    const int32_t *seq_lens,
+    int32_t n_requests, int32_t query_len, int32_t max_seq_len,
+    const float *w,
+    const void *mask, int64_t mask_stride_t,
+    int32_t n_heads, int32_t head_dim,
+    int32_t k_top, int32_t *idx, float *val, int64_t out_stride,
+    void *stream);
+
+/*
  * Bytes of device workspace an operation needs (0 if none).  For the fused
  * operations n_rows/n_cols are the score rows and columns (n_tokens x n_pool,
  * or n_requests*query_len x max_seq_len).  Returns (size_t)-1 for negative

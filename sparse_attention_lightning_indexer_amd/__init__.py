@@ -28,8 +28,9 @@ EXPORTS = (
     "indexer_abi_version", "indexer_status_string", "indexer_last_error",
     "indexer_score_prefill", "indexer_score_decode", "indexer_topk",
     "indexer_score_topk_fused_prefill", "indexer_score_topk_fused_decode",
-    "indexer_workspace_bytes",
+    "indexer_workspace_bytes", "indexer_score_topk_fused_decode_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class IndexerError(RuntimeError):
@@ -79,6 +80,10 @@ def load_library(path: str = LIB_PATH):
                                                     i32, i32, i32, p, p, i64, i32, i32,
                                                     i32, p, p, i64, p, sz, p]
     lib.indexer_score_topk_fused_decode.restype = st
+    lib.indexer_score_topk_fused_decode_noalloc.argtypes = [p, i64, i64, p, i32, i64, p, i64, p,
+                                                            i32, i32, i32, p, p, i64, i32, i32,
+                                                            i32, p, p, i64, p]
+    lib.indexer_score_topk_fused_decode_noalloc.restype = st
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -331,8 +336,44 @@ def score_topk_fused_decode(q, k_cache, block_table, seq_lens, query_len: int,
     return idx, val
 
 
+def score_topk_fused_decode_noalloc(q, k_cache, block_table, seq_lens, query_len: int,
+                                    max_seq_len: int, w, k_top: int, mask=None, idx=None, val=None):
+    """score_topk_fused_decode without a workspace: the library keeps the
+    score rows in its static per-GPU scratch (at most NOALLOC_SCRATCH_BYTES;
+    larger calls raise).  Calls that overlap on one GPU race.  `idx` (and
+    `val`, or None for no values) must be given when the caller cannot
+    allocate; otherwise they are allocated here."""
+    torch = _torch()
+    lib = load_library()
+    dev = _q_checks(q, w)
+    RQ, H, d = q.shape
+    bs = _paged_checks(q, k_cache, block_table, seq_lens, dev, max_seq_len)
+    R = seq_lens.shape[0]
+    if RQ != R * query_len:
+        raise ValueError(f"q has {RQ} rows, expected n_requests*query_len = {R * query_len}")
+    if mask is not None:
+        _need(mask, "mask", torch.float16, dev, 2)
+        if mask.stride(1) != 1 or tuple(mask.shape) != (RQ, max_seq_len):
+            raise ValueError("mask must be [R*Q, max_seq_len] with contiguous rows")
+    if idx is None:
+        idx = torch.empty((RQ, k_top), dtype=torch.int32, device=dev)
+        if val is None:
+            val = torch.empty((RQ, k_top), dtype=torch.float32, device=dev)
+    for o in (idx, val):
+        if o is not None and (tuple(o.shape) != (RQ, k_top) or not o.is_contiguous()):
+            raise ValueError(f"outputs must be contiguous [{RQ}, {k_top}]")
+    if RQ == 0:
+        return idx, val
+    _check(lib.indexer_score_topk_fused_decode_noalloc(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), bs, k_cache.stride(1),
+        _ptr(block_table), block_table.stride(0), _ptr(seq_lens), R, query_len,
+        max_seq_len, _ptr(w), _ptr(mask), mask.stride(0) if mask is not None else 0,
+        H, d, k_top, _ptr(idx), _ptr(val), k_top, _stream(dev)))
+    return idx, val
+
+
 __all__ = [
     "score_prefill", "score_decode", "topk", "score_topk_fused_prefill",
-    "score_topk_fused_decode", "workspace_bytes", "load_library", "IndexerError",
+    "score_topk_fused_decode", "score_topk_fused_decode_noalloc", "workspace_bytes", "load_library", "IndexerError",
     "EXPORTS", "MAX_K_TOP",
 ]

@@ -226,6 +226,57 @@ indexer_status run_topk(const float *score, int64_t score_stride_t, int32_t n_ro
     return hip_status(lidx::launch_topk(t, workspace, stream), "top-k kernel launch");
 }
 
+// Score decode into `workspace` (fused_bytes(...) bytes, 256-byte aligned),
+// then the top-k of its rows; arguments already checked.
+indexer_status fused_decode(const void *q, int64_t q_stride_t, int64_t q_stride_h, const void *k_cache,
+                            int32_t block_size, int64_t k_stride_s, const int32_t *block_table, int64_t bt_stride,
+                            const int32_t *seq_lens, int32_t n_requests, int32_t query_len, int32_t max_seq_len,
+                            const float *w, const void *mask, int64_t mask_stride_t, int32_t n_heads,
+                            int32_t head_dim, int32_t k_top, int32_t *idx, float *val, int64_t out_stride,
+                            void *workspace, hipStream_t s) {
+    const int32_t n_rows = n_requests * query_len;
+    const int64_t row = (int64_t)round_up((size_t)max_seq_len, 4);
+    float *scores = (float *)workspace;
+    void *topk_ws = (char *)workspace + round_up((size_t)row * 4 * n_rows, 256);
+    if (max_seq_len > 0) {
+        lidx::ScoreArgs a = decode_args(q, q_stride_t, q_stride_h, k_cache, block_size, k_stride_s, block_table,
+                                        bt_stride, seq_lens, n_requests, query_len, max_seq_len, w, mask,
+                                        mask_stride_t, scores, row);
+        indexer_status st = run_score(a, n_heads, head_dim, true, n_requests, s);
+        if (st != INDEXER_OK) return st;
+    }
+    return run_topk(scores, row, n_rows, max_seq_len, nullptr, k_top, idx, val, out_stride, topk_ws, s);
+}
+
+// Scratch of the no-allocation fused decode: a static device array, one copy
+// per GPU, held until the process ends.  In host code its name is only a
+// stand-in for the device copies, so the device address is looked up once per
+// device (with that device current) and kept; only that address is ever
+// passed to a kernel.  Every entry the top-k reads is written by the score
+// kernel first, so nothing in it needs clearing between calls.
+static __device__ __attribute__((aligned(256))) unsigned char scratch[INDEXER_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+indexer_status scratch_address(void **out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(INDEXER_EHIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(INDEXER_EHIP, "device %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p)
+            return fail(INDEXER_EHIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return INDEXER_OK;
+}
+
 }  // namespace
 
 namespace lidx {
@@ -370,17 +421,34 @@ indexer_status indexer_score_topk_fused_decode(const void *q, int64_t q_stride_t
         return fail(INDEXER_EWORKSPACE, "fused decode needs %zu bytes of 256-byte aligned workspace, got %zu", need,
                     workspace ? workspace_bytes : 0);
     if (n_rows == 0) return ok();
-    const int64_t row = (int64_t)round_up((size_t)max_seq_len, 4);
-    float *scores = (float *)workspace;
-    void *topk_ws = (char *)workspace + round_up((size_t)row * 4 * n_rows, 256);
-    hipStream_t s = (hipStream_t)stream;
-    if (max_seq_len > 0) {
-        lidx::ScoreArgs a = decode_args(q, q_stride_t, q_stride_h, k_cache, block_size, k_stride_s, block_table,
-                                        bt_stride, seq_lens, n_requests, query_len, max_seq_len, w, mask,
-                                        mask_stride_t, scores, row);
-        if ((st = run_score(a, n_heads, head_dim, true, n_requests, s)) != INDEXER_OK) return st;
-    }
-    return run_topk(scores, row, n_rows, max_seq_len, nullptr, k_top, idx, val, out_stride, topk_ws, s);
+    return fused_decode(q, q_stride_t, q_stride_h, k_cache, block_size, k_stride_s, block_table, bt_stride,
+                        seq_lens, n_requests, query_len, max_seq_len, w, mask, mask_stride_t, n_heads, head_dim,
+                        k_top, idx, val, out_stride, workspace, (hipStream_t)stream);
+}
+
+indexer_status indexer_score_topk_fused_decode_noalloc(
+    const void *q, int64_t q_stride_t, int64_t q_stride_h, const void *k_cache, int32_t block_size,
+    int64_t k_stride_s, const int32_t *block_table, int64_t bt_stride, const int32_t *seq_lens, int32_t n_requests,
+    int32_t query_len, int32_t max_seq_len, const float *w, const void *mask, int64_t mask_stride_t,
+    int32_t n_heads, int32_t head_dim, int32_t k_top, int32_t *idx, float *val, int64_t out_stride, void *stream) {
+    indexer_status st = check_decode(q, q_stride_t, q_stride_h, k_cache, block_size, k_stride_s, block_table,
+                                     bt_stride, seq_lens, n_requests, query_len, max_seq_len, w, mask,
+                                     mask_stride_t, n_heads, head_dim);
+    if (st != INDEXER_OK) return st;
+    if ((st = check_topk_out(k_top, idx, val, out_stride)) != INDEXER_OK) return st;
+    const int32_t n_rows = n_requests * query_len;
+    const size_t need = fused_bytes(n_rows, max_seq_len, k_top);
+    if (need > INDEXER_NOALLOC_SCRATCH_BYTES)
+        return fail(INDEXER_EWORKSPACE,
+                    "no-allocation fused decode needs %zu bytes of scratch for %d rows of %d keys; its static "
+                    "scratch holds %zu (INDEXER_NOALLOC_SCRATCH_BYTES)",
+                    need, n_rows, max_seq_len, (size_t)INDEXER_NOALLOC_SCRATCH_BYTES);
+    if (n_rows == 0) return ok();
+    void *ptr = nullptr;
+    if ((st = scratch_address(&ptr)) != INDEXER_OK) return st;
+    return fused_decode(q, q_stride_t, q_stride_h, k_cache, block_size, k_stride_s, block_table, bt_stride,
+                        seq_lens, n_requests, query_len, max_seq_len, w, mask, mask_stride_t, n_heads, head_dim,
+                        k_top, idx, val, out_stride, ptr, (hipStream_t)stream);
 }
 
 }  // extern "C"

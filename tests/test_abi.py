@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 9, names
+    assert len(names) == 10, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(li.EXPORTS)
