@@ -52,8 +52,8 @@ MALL_BYTES = 256 << 20
 CSRC = os.path.join(ROOT, "sparse_attention_lightning_indexer_amd", "csrc")
 # sources whose change makes a stored byte count stale, per kernel
 KERNEL_SOURCES = {
-    "score": ["decode_kernel.hip", "score_kernel.hip", "device_common.h", "internal.h", "indexer_api.hip"],
-    "topk": ["topk_kernel.hip", "device_common.h", "internal.h", "indexer_api.hip"],
+    "score": ["decode_kernel.hip", "score_kernel.hip", "device_common.h", "internal.h"],
+    "topk": ["topk_kernel.hip", "device_common.h", "internal.h"],
 }
 TRAFFIC_MARK = "traffic-record:"
 
@@ -144,6 +144,49 @@ def pmc_summary(config: str, fetch_dir: str, write_dir: str, calib_mib: int) -> 
     return txt
 
 
+def mfma_summary(config: str, counter_dir: str) -> str:
+    """Markdown summary of a rocprofv3 --pmc run of this benchmark with the
+    MFMA counters (SQ_INSTS_VALU_MFMA_MOPS_F16, SQ_VALU_MFMA_BUSY_CYCLES,
+    GRBM_GUI_ACTIVE, SQ_BUSY_CYCLES) and --kernel-trace: per kernel the mean
+    per dispatch, the f16 MFMA flops the hardware counted (MOPS x 512), the
+    MFMA busy fraction (busy cycles over GPU-active cycles x SIMDs), and the
+    achieved shader clock (active cycles per XCD over the dispatch time)."""
+    import csv
+    import glob
+
+    vals, dur = {}, {}
+    for path in glob.glob(os.path.join(counter_dir, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                key = (r["Kernel_Name"], r["Counter_Name"])
+                vals.setdefault(key, []).append(float(r["Counter_Value"]))
+    for path in glob.glob(os.path.join(counter_dir, "**", "*kernel_trace.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                dur.setdefault(r["Kernel_Name"], []).append(
+                    (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-9)
+    kernels = sorted({k for k, _ in vals if kernel_role(k) == "score"})
+    n_simd, n_xcd = 1024, 8
+    out = [f"| kernel | dispatches | MFMA f16 TFLOP counted | MFMA busy | active cycles/XCD | "
+           f"dispatch us | shader clock GHz | counted TFLOP/s |", "|---|---|---|---|---|---|---|---|"]
+    for k in kernels:
+        def mean(c):
+            v = vals.get((k, c))
+            return sum(v) / len(v) if v else float("nan")
+        mops = mean("SQ_INSTS_VALU_MFMA_MOPS_F16")
+        busy = mean("SQ_VALU_MFMA_BUSY_CYCLES")
+        act = mean("GRBM_GUI_ACTIVE")
+        n = len(vals.get((k, "GRBM_GUI_ACTIVE"), []))
+        d = dur.get(k)
+        us = sum(d) / len(d) * 1e6 if d else float("nan")
+        flops = mops * 512
+        cyc = act / n_xcd
+        short = k if len(k) < 70 else k[:67] + "..."
+        out.append(f"| `{short}` | {n} | {flops / 1e12:.1f} | {busy / (cyc * n_simd):.3f} | {cyc:.4g} | "
+                   f"{us:.1f} | {cyc / (us * 1e3):.2f} | {flops / (us * 1e-6) / 1e12:.0f} |")
+    return "\n".join(out) + "\n"
+
+
 def trace_summary(trace_dir: str) -> str:
     """Markdown table of the kernel statistics of a rocprofv3
     --kernel-trace --stats run (the *kernel_stats.csv it writes)."""
@@ -176,6 +219,9 @@ def parse():
     ap.add_argument("--pmc-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"), default=None,
                     help="print the markdown summary of two rocprofv3 --pmc runs of this benchmark "
                          "(FETCH_SIZE, WRITE_SIZE) for --config and exit; needs no GPU")
+    ap.add_argument("--mfma-summary", metavar="COUNTER_DIR", default=None,
+                    help="print the markdown summary of a rocprofv3 --pmc run with the MFMA counters "
+                         "(and --kernel-trace) for --config and exit; needs no GPU")
     ap.add_argument("--trace-summary", metavar="TRACE_DIR", default=None,
                     help="print the kernel table of a rocprofv3 --kernel-trace --stats run and exit")
     ap.add_argument("--no-peak-probe", action="store_true",
@@ -229,6 +275,9 @@ def main():
     args = parse()
     if args.trace_summary:
         print(trace_summary(args.trace_summary))
+        return
+    if args.mfma_summary:
+        print(mfma_summary(args.config, args.mfma_summary))
         return
     if args.pmc_summary:
         print(pmc_summary(args.config, args.pmc_summary[0], args.pmc_summary[1], args.calib_copy_mib or 1024))

@@ -34,12 +34,18 @@
  *    -inf and NaN are never selected and -0 ties with +0.  Rows with fewer
  *    than k_top selectable keys are padded with index -1 and value -inf.
  *  - Supported shapes (others return INDEXER_ENOTSUP, as a backend's
- *    supports_op check would): 1 <= n_heads <= 64; head_dim in {64, 128};
- *    1 <= k_top <= INDEXER_MAX_K_TOP.  Kernels are compiled for 4, 8, 16, 32
- *    and 64 heads; other counts run as the next of those with the last head
- *    tile zero-filled (the b11372 notes' Metal kernel does the same): the
- *    extra heads read a real head's q and weigh exactly zero, and no byte past
- *    q's or w's n_heads heads is read.
+ *    supports_op check would): 1 <= n_heads <= 1024; head_dim a multiple of
+ *    8 in [8, 256]; 1 <= k_top <= INDEXER_MAX_K_TOP.  Kernels are compiled
+ *    for 4, 8, 16, 32 and 64 heads and head dimensions 64, 128 and 256:
+ *      - other head counts run as the next compiled one with the last head
+ *        tile zero-filled (the b11372 notes' Metal kernel does the same): the
+ *        extra heads read a real head's q and weigh exactly zero;
+ *      - other head dimensions run zero-padded to the next compiled one (the
+ *        padded q and key elements are 0, so every dot product is unchanged);
+ *      - more than 64 heads (32 at head dimensions above 128) run as passes
+ *        over head groups, each adding its rectified, weighted head sum into
+ *        the same score rows in place; the mask is added once, by the last.
+ *    No byte past q's or w's n_heads heads or a row's head_dim is read.
  *  - Alignment: q, k (or k_cache) and every q/k row must be 16-byte aligned
  *    (strides multiples of 8 elements); score and w 4-byte aligned.
  *  - Thread safety: every entry point may be called from any host thread;

@@ -105,8 +105,9 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(ScoreArgs a) {
             const int head = head0 + mb * (SPLIT ? 16 : G::HPB);
             const _Float16 *src = a.q + (int64_t)t * a.q_st + (int64_t)real_head(head, a.n_heads) * a.q_sh + kh * (D / 2);
 #pragma unroll
-            for (int kk = 0; kk < G::KSTEPS; ++kk)
-                qa[mb][kk] = ok ? *reinterpret_cast<const half8 *>(src + kk * 8) : half8{};
+            for (int kk = 0; kk < G::KSTEPS; ++kk)  // zero past the real head dimension
+                qa[mb][kk] = ok && kh * (D / 2) + kk * 8 < a.head_dim ? *reinterpret_cast<const half8 *>(src + kk * 8)
+                                                                     : half8{};
         }
     }
     // weights: SGPR operands in the general mapping; per-lane registers when
@@ -191,6 +192,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(ScoreArgs a) {
                 const int64_t phys = bt_lds[blk - b_lo];
                 src = a.k + (phys * bs + slot) * a.k_ss + lc * 8;
             }
+            if (lc * 8 >= a.head_dim) src = reinterpret_cast<const _Float16 *>(kZeroChunk);  // padded tile
             dma16(src, base + (it * kWaves + wid) * 1024);
         }
     }
@@ -239,7 +241,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(ScoreArgs a) {
 #pragma unroll
                         for (int r = 0; r < 16; ++r) sum = fmaf(relu(acc[mb][r]), wv[mb][r], sum);
                     sum += __shfl_xor(sum, 32, 64);
-                    if (vis[0]) res[i][0] = sum + (float)mv[i][0];
+                    if (vis[0]) res[i][0] = a.add_mask ? sum + (float)mv[i][0] : sum;
                 } else {
 #pragma unroll
                     for (int j = 0; j < SLOTS; ++j) {
@@ -249,7 +251,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(ScoreArgs a) {
 #pragma unroll
                             for (int rr = 0; rr < 4 * G::G; ++rr)
                                 sum = fmaf(relu(acc[mb][4 * G::G * j + rr]), head_weight(wc, mb * G::HPB + rr, a.n_heads), sum);
-                        if (vis[j]) res[i][j] = sum + (float)mv[i][j];
+                        if (vis[j]) res[i][j] = a.add_mask ? sum + (float)mv[i][j] : sum;
                     }
                 }
             }
@@ -263,8 +265,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(ScoreArgs a) {
         if (i < n_tiles && s < key_hi) {
 #pragma unroll
             for (int j = 0; j < SLOTS; ++j)
-                if (out_t[j] < row_hi && (!SPLIT || kh == 0))
-                    a.score[(int64_t)out_t[j] * a.score_st + s] = res[i][j];
+                if (out_t[j] < row_hi && (!SPLIT || kh == 0)) {
+                    float *dst = a.score + (int64_t)out_t[j] * a.score_st + s;
+                    // a later pass over more heads adds to the stored partial
+                    // sum (-inf stays -inf)
+                    *dst = a.accumulate ? res[i][j] + *dst : res[i][j];
+                }
         }
     }
     const int fill_lo = min(key_lo + n_tiles * NK, key_hi);
@@ -1033,7 +1039,10 @@ hipError_t launch_hd(const ScoreArgs &a, const ScorePlan &p, bool split, hipStre
 
 template <int H>
 hipError_t launch_h(const ScoreArgs &a, const ScorePlan &p, int D, bool split, hipStream_t stream) {
-    return D == 64 ? launch_hd<H, 64>(a, p, split, stream) : launch_hd<H, 128>(a, p, split, stream);
+    if (D == 64) return launch_hd<H, 64>(a, p, split, stream);
+    if (D == 128) return launch_hd<H, 128>(a, p, split, stream);
+    if constexpr (H <= 32) return launch_hd<H, 256>(a, p, split, stream);  // a pass holds 32 heads at 256
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -1046,7 +1055,11 @@ ScorePlan plan_decode(ScoreArgs &a, int n_heads, int head_dim, int n_requests) {
     // head mapping); fewer heads pack 32/heads rows per M-block
     // the mask travels in 8-key (16-byte) chunks: aligned rows, whole chunks
     const bool mask_ok = a.mask == nullptr || (a.mask_vec && a.n_cols >= 8 && a.n_cols % 8 == 0);
-    if (mask_ok && a.block_size >= 4 && n_requests <= kMaxRG) {
+    // the persistent kernel runs single passes at the exact tile widths 64
+    // and 128; padded head dimensions, 256 and multi-pass head groups take
+    // the chunked kernel
+    const bool shape_ok = head_dim <= 128 && a.head_dim == head_dim && !a.accumulate && a.add_mask;
+    if (shape_ok && mask_ok && a.block_size >= 4 && n_requests <= kMaxRG) {
         const bool split = n_heads >= 32;
         const int tpb = split ? 1 : 32 / (n_heads < 16 ? n_heads : 16);
         int ng = 1;

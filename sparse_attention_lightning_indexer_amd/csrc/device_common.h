@@ -20,7 +20,7 @@ typedef const __attribute__((address_space(4))) int32_t const_i32;
 template <int H, int D>
 struct Geo {
     static_assert(H == 4 || H == 8 || (H % 16 == 0 && H <= 64), "head count");
-    static_assert(D == 64 || D == 128, "head dim");
+    static_assert(D == 64 || D == 128 || D == 256, "head dim");
     static constexpr int HPB = H < 16 ? H : 16;   // heads per M-block
     static constexpr int TPB = 32 / HPB;          // query rows per M-block
     static constexpr int MBLK = H / HPB;          // M-blocks covering all heads
@@ -29,16 +29,23 @@ struct Geo {
     static constexpr int KSTEPS = D / 16;         // MFMA K steps
     static constexpr int CPR = D / 8;             // 16-byte chunks per key row
     static constexpr int ROWB = 2 * D;            // bytes per key row in LDS
-    static constexpr int ROWS_PER_256B = 256 / ROWB;
+    static constexpr int ROWS_PER_256B = ROWB < 256 ? 256 / ROWB : 1;
+    static constexpr int SWZ_MASK = CPR < 16 ? CPR - 1 : 15;
 };
 
 // Swizzled position of a key row's 16-byte chunk in LDS: the chunk index is
 // XORed with a function of the row so that the rows read by one 16-lane
-// phase land in distinct 16-byte bank groups.
+// phase land in distinct 16-byte bank groups (the 64 banks span 256 bytes;
+// 16 consecutive rows of 128, 256 or 512 bytes then hit 16 different groups).
 template <int D>
 __device__ __forceinline__ int swz(int n) {
-    return (n / Geo<4, D>::ROWS_PER_256B) & (Geo<4, D>::CPR - 1);
+    return (n / Geo<4, D>::ROWS_PER_256B) & Geo<4, D>::SWZ_MASK;
 }
+
+// Sixteen zero bytes in device memory: the source of the key chunks past a
+// head dimension that is shorter than the compiled tile (its q chunks are
+// zero too, so the padded part of every dot product is exactly 0).
+static __device__ __attribute__((aligned(16))) const unsigned int kZeroChunk[4] = {0u, 0u, 0u, 0u};
 
 // A value the caller knows to be the same in every lane (an LDS word read at
 // a uniform address, say), moved to a scalar register so that the arithmetic

@@ -49,8 +49,9 @@ size_t round_up(size_t v, size_t m) { return (v + m - 1) / m * m; }
 indexer_status check_q_w(const void *q, int64_t q_stride_t, int64_t q_stride_h, const float *w,
                          int32_t n_heads, int32_t head_dim) {
     if (!lidx::score_shape_supported(n_heads, head_dim))
-        return fail(INDEXER_ENOTSUP, "n_heads=%d head_dim=%d not supported (n_heads in 1..64, head_dim in {64,128})",
-                    n_heads, head_dim);
+        return fail(INDEXER_ENOTSUP,
+                    "n_heads=%d head_dim=%d not supported (n_heads in 1..%d, head_dim a multiple of 8 in 8..256)",
+                    n_heads, head_dim, lidx::kMaxHeads);
     if (!q) return fail(INDEXER_EINVAL, "q is NULL");
     if (!w) return fail(INDEXER_EINVAL, "w is NULL");
     if (!aligned(q, 16)) return fail(INDEXER_EINVAL, "q must be 16-byte aligned");
@@ -196,18 +197,36 @@ lidx::ScoreArgs decode_args(const void *q, int64_t q_stride_t, int64_t q_stride_
     return a;
 }
 
-indexer_status run_score(lidx::ScoreArgs &a, int n_heads_real, int head_dim, bool paged, int n_requests,
+// The score kernels hold up to 64 heads (32 at head dimension 256) of one
+// row's q in registers.  More heads run as passes over head groups: each
+// pass adds its groups' rectified, weighted head sum into the same score
+// rows (the b11372 notes' in-place sum over heads, a group at a time), and
+// the last pass adds the mask.  A head dimension other than 64, 128 or 256
+// runs zero-padded to the next of them.
+indexer_status run_score(const lidx::ScoreArgs &base, int n_heads_real, int head_dim, bool paged, int n_requests,
                          hipStream_t stream) {
-    // the kernels run the next compiled head count; the extra heads weigh 0
-    a.n_heads = n_heads_real;
-    const int n_heads = lidx::compiled_heads(n_heads_real);
-    lidx::ScorePlan p = paged ? lidx::plan_decode(a, n_heads, head_dim, n_requests)
-                              : lidx::plan_score(a, n_heads, head_dim);
-    if ((int64_t)a.n_row_groups * a.n_chunks > INT32_MAX)
-        return fail(INDEXER_EINVAL, "problem too large for one launch");
-    hipError_t e = paged ? lidx::launch_decode(a, p, n_heads, head_dim, stream)
-                         : lidx::launch_score(a, p, n_heads, head_dim, stream);
-    return hip_status(e, "score kernel launch");
+    const int dpad = lidx::compiled_dim(head_dim);
+    const int per_pass = lidx::pass_heads(dpad);
+    for (int lo = 0; lo < n_heads_real; lo += per_pass) {
+        lidx::ScoreArgs a = base;
+        const int cnt = n_heads_real - lo < per_pass ? n_heads_real - lo : per_pass;
+        a.q = base.q + (int64_t)lo * base.q_sh;
+        a.w = base.w + lo;
+        a.n_heads = cnt;  // the kernels run the next compiled head count; the extra heads weigh 0
+        a.head_dim = head_dim;
+        a.accumulate = lo > 0;
+        a.add_mask = lo + cnt >= n_heads_real;
+        const int n_heads = lidx::compiled_heads(cnt);
+        lidx::ScorePlan p = paged ? lidx::plan_decode(a, n_heads, dpad, n_requests)
+                                  : lidx::plan_score(a, n_heads, dpad);
+        if ((int64_t)a.n_row_groups * a.n_chunks > INT32_MAX)
+            return fail(INDEXER_EINVAL, "problem too large for one launch");
+        hipError_t e = paged ? lidx::launch_decode(a, p, n_heads, dpad, stream)
+                             : lidx::launch_score(a, p, n_heads, dpad, stream);
+        indexer_status st = hip_status(e, "score kernel launch");
+        if (st != INDEXER_OK) return st;
+    }
+    return ok();
 }
 
 indexer_status run_topk(const float *score, int64_t score_stride_t, int32_t n_rows, int32_t n_cols,

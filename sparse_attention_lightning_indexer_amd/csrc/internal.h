@@ -23,7 +23,10 @@ struct ScoreArgs {
     int32_t bs_shift;           // log2(block_size) if a power of two, else -1
     const int32_t *seq_lens;    // paged only
     const float *w;
-    int32_t n_heads;            // heads of q and w; the kernel's tile may be larger (extra heads weigh 0)
+    int32_t n_heads;            // heads of q and w (of this pass); the kernel's tile may be larger (extra heads weigh 0)
+    int32_t head_dim;           // real head dimension (multiple of 8); the kernel's tile may be wider (zero tail)
+    int32_t accumulate;         // add this pass's head sum to the score already stored (visible entries)
+    int32_t add_mask;           // add the mask's finite values (the last pass only)
     const _Float16 *mask;
     int64_t mask_st;
     const int32_t *vis_len;     // contiguous only (nullable)
@@ -54,6 +57,17 @@ struct ScorePlan {
 bool score_shape_supported(int n_heads, int head_dim);
 // The smallest compiled head count (4, 8, 16, 32, 64) holding n_heads.
 int compiled_heads(int n_heads);
+// Largest head count and supported head dimensions: head_dim a multiple of 8
+// in [8, 256]; n_heads in [1, kMaxHeads].  Kernels are compiled for head
+// dimensions 64, 128 and 256 (others run zero-padded to the next) and for up
+// to 64 heads per pass (32 at 256); more heads run as several passes that
+// accumulate into the same score rows.
+constexpr int kMaxHeads = 1024;
+// Head dimension padded to a compiled tile width, and the heads one pass of
+// a score kernel covers at that width (the q fragments of a pass stay in
+// registers: 64 heads at up to 128 dimensions, 32 at 256).
+constexpr int compiled_dim(int d) { return d <= 64 ? 64 : (d <= 128 ? 128 : 256); }
+constexpr int pass_heads(int dpad) { return dpad <= 128 ? 64 : 32; }
 // Contiguous keys (score_kernel.hip).  Fills the launch-geometry fields of
 // `a` and returns the plan.
 ScorePlan plan_score(ScoreArgs &a, int n_heads, int head_dim);

@@ -47,8 +47,11 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 
-// PAD: fewer real heads than H (the extra heads weigh 0).  Kept a separate
-// instance so that the full-head kernel's weights stay plain scalar loads.
+// PAD: the general instance -- fewer real heads than H (the extra heads
+// weigh 0), a head dimension below D (zero tail), or one pass of several over
+// head groups (accumulate into the stored sums; the mask on the last pass).
+// Kept separate so that the exact-shape kernel keeps its weights as plain
+// scalar loads and carries none of these checks.
 template <int H, int D, int NBW, bool PAD>
 __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
     using G = Geo<H, D>;
@@ -160,7 +163,8 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
                                   kh * (D / 2);
 #pragma unroll
             for (int kk = 0; kk < G::KSTEPS; ++kk) {
-                if (ok) {
+                // elements past the real head dimension are zero (padded tile)
+                if (ok && (!PAD || kh * (D / 2) + kk * 8 < a.head_dim)) {
                     qa[mb][kk] = *reinterpret_cast<const half8 *>(src + kk * 8);
                 } else {
                     qa[mb][kk] = half8{};
@@ -182,6 +186,8 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
 
     auto key_src = [&](int s) -> const _Float16 * { return a.k + (int64_t)s * a.k_ss; };
 
+    // chunks past the real head dimension come from a zero chunk
+    const bool dim_tail = PAD && a.head_dim < D;
     auto issue_tile = [&](int tile, int buf) {
         const int s0 = key_lo + tile * NK;
         unsigned char *base = smem + buf * tile_bytes;
@@ -192,6 +198,7 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
             const int lc = (c & (G::CPR - 1)) ^ swz<D>(n);
             const int s = s0 + n;
             const _Float16 *src = s < load_limit ? key_src(s) + lc * 8 : a.k;
+            if (dim_tail && lc * 8 >= a.head_dim) src = reinterpret_cast<const _Float16 *>(kZeroChunk);
             __builtin_amdgcn_global_load_lds(
                 src, (__attribute__((address_space(3))) void *)(base + (it * kWaves + wid) * 1024),
                 16, 0, 0);
@@ -225,7 +232,12 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
             if (s < key_hi) {
 #pragma unroll
                 for (int j = 0; j < G::SLOTS; ++j)
-                    if (out_t[j] < row_hi) a.score[(int64_t)out_t[j] * a.score_st + s] = pend[nb][j];
+                    if (out_t[j] < row_hi) {
+                        float *dst = a.score + (int64_t)out_t[j] * a.score_st + s;
+                        // a later pass over more heads adds to the stored
+                        // partial sum (-inf stays -inf)
+                        *dst = PAD && a.accumulate ? pend[nb][j] + *dst : pend[nb][j];
+                    }
             }
         }
     };
@@ -295,7 +307,7 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
                         for (int rr = 0; rr < 4 * G::G; ++rr)
                             sum = fmaf(relu(acc[mb][4 * G::G * j + rr]),
                                        PAD ? head_weight(wc, mb * G::HPB + rr, a.n_heads) : wc[mb * G::HPB + rr], sum);
-                    if (vis[j]) res[j] = sum + (float)mcur[nb][j];
+                    if (vis[j]) res[j] = !PAD || a.add_mask ? sum + (float)mcur[nb][j] : sum;
                 }
             }
 #pragma unroll
@@ -352,22 +364,33 @@ hipError_t launch_one(const ScoreArgs &a, const ScorePlan &p, hipStream_t stream
     return hipGetLastError();
 }
 
+template <int H, int D, bool PAD>
+hipError_t launch_nbw(const ScoreArgs &a, const ScorePlan &p, hipStream_t stream) {
+    if constexpr (D == 256) {
+        return p.nbw == 2 ? launch_one<H, D, 2, PAD>(a, p, stream) : launch_one<H, D, 1, PAD>(a, p, stream);
+    } else {
+        return p.nbw == 4 ? launch_one<H, D, 4, PAD>(a, p, stream) : launch_one<H, D, 1, PAD>(a, p, stream);
+    }
+}
+
 template <int H, int D>
 hipError_t launch_hd(const ScoreArgs &a, const ScorePlan &p, hipStream_t stream) {
-    if (a.n_heads == H)
-        return p.nbw == 4 ? launch_one<H, D, 4, false>(a, p, stream) : launch_one<H, D, 1, false>(a, p, stream);
-    return p.nbw == 4 ? launch_one<H, D, 4, true>(a, p, stream) : launch_one<H, D, 1, true>(a, p, stream);
+    if (a.n_heads == H && a.head_dim == D && !a.accumulate && a.add_mask) return launch_nbw<H, D, false>(a, p, stream);
+    return launch_nbw<H, D, true>(a, p, stream);
 }
 
 template <int H>
 hipError_t launch_h(const ScoreArgs &a, const ScorePlan &p, int D, hipStream_t stream) {
-    return D == 64 ? launch_hd<H, 64>(a, p, stream) : launch_hd<H, 128>(a, p, stream);
+    if (D == 64) return launch_hd<H, 64>(a, p, stream);
+    if (D == 128) return launch_hd<H, 128>(a, p, stream);
+    if constexpr (H <= 32) return launch_hd<H, 256>(a, p, stream);  // a pass holds 32 heads at 256
+    return hipErrorInvalidValue;
 }
 
 }  // namespace
 
 bool score_shape_supported(int n_heads, int head_dim) {
-    return n_heads >= 1 && n_heads <= 64 && (head_dim == 64 || head_dim == 128);
+    return n_heads >= 1 && n_heads <= kMaxHeads && head_dim >= 8 && head_dim <= 256 && head_dim % 8 == 0;
 }
 
 int compiled_heads(int n_heads) {
@@ -385,7 +408,8 @@ ScorePlan plan_score(ScoreArgs &a, int n_heads, int head_dim) {
     int ng = 1;
     while (ng < kWaves && ng * tpb < rows) ng *= 2;
     p.nc = kWaves / ng;
-    p.nbw = p.nc == 1 ? 4 : 1;
+    // 32 KB key tiles: 128 keys of 128 dimensions (64 at 256)
+    p.nbw = p.nc == 1 ? (head_dim == 256 ? 2 : 4) : 1;
     p.tile_keys = 32 * p.nc * p.nbw;
     p.rows_per_group = ng * tpb;
     a.nc = p.nc;

@@ -64,9 +64,11 @@ def prefill(lib, **kw):
 
 @pytest.mark.parametrize("kw,status,msg", [
     (dict(H=0), li.ENOTSUP, b"n_heads=0"),
-    (dict(H=65), li.ENOTSUP, b"n_heads=65"),
-    (dict(H=128), li.ENOTSUP, b"not supported"),
-    (dict(d=96, qsh=96, qst=96 * 64, kss=96), li.ENOTSUP, b"head_dim=96"),
+    (dict(H=1025), li.ENOTSUP, b"n_heads=1025"),
+    (dict(H=-3), li.ENOTSUP, b"not supported"),
+    (dict(d=100, qsh=104, qst=104 * 64, kss=104), li.ENOTSUP, b"head_dim=100"),
+    (dict(d=264, qsh=264, qst=264 * 64, kss=264), li.ENOTSUP, b"head_dim=264"),
+    (dict(d=0, qsh=8, qst=8 * 64, kss=8), li.ENOTSUP, b"head_dim=0"),
     (dict(q=None), li.EINVAL, b"q is NULL"),
     (dict(k=None), li.EINVAL, b"k is NULL"),
     (dict(w=None), li.EINVAL, b"w is NULL"),
@@ -107,7 +109,7 @@ def decode(lib, **kw):
     (dict(bt=None), li.EINVAL, b"block_table is NULL"),
     (dict(sl=None), li.EINVAL, b"seq_lens is NULL"),
     (dict(kc=None), li.EINVAL, b"k_cache is NULL"),
-    (dict(H=96), li.ENOTSUP, b"n_heads=96"),
+    (dict(H=2000), li.ENOTSUP, b"n_heads=2000"),
     (dict(sst=100), li.EINVAL, b"score_stride_t"),
     (dict(R=70000, Q=70000), li.EINVAL, b"int32"),
 ])

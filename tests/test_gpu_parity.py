@@ -192,6 +192,58 @@ def test_any_head_count(kind, H, d, shape):
     _full_check(inp, f"{kind} H={H} d={d}")
 
 
+# Head dimensions off the compiled tile widths (run zero-padded to 64, 128 or
+# 256) and head counts past one pass (64 heads, or 32 at 256 dimensions: the
+# passes add their head groups' sums into the same score rows, the last one
+# adds the mask).
+WIDE_CASES = [
+    # kind, H, d, (prefill T, P) or (decode R, Q, lo, hi), mask
+    ("prefill", 4, 8, (9, 130), "random"),
+    ("prefill", 16, 48, (21, 333), "bias"),
+    ("prefill", 64, 96, (17, 257), "causal"),
+    ("prefill", 8, 136, (13, 300), "random"),
+    ("prefill", 32, 192, (19, 400), "bias"),
+    ("prefill", 20, 256, (11, 270), "random"),
+    ("prefill", 64, 256, (9, 300), "bias"),      # two passes of 32 heads at 256
+    ("prefill", 65, 128, (15, 333), "bias"),     # two passes: 64 + 1
+    ("prefill", 128, 64, (12, 250), "causal"),
+    ("prefill", 200, 80, (7, 180), "bias"),      # four passes, padded dimension
+    ("decode", 64, 96, (20, 1, 1, 700), "none"),
+    ("decode", 32, 256, (10, 4, 4, 600), "bias"),
+    ("decode", 96, 128, (12, 2, 2, 900), "bias"),
+    ("decode", 130, 40, (8, 3, 3, 500), "random"),
+    ("decode", 8, 200, (16, 1, 1, 300), "none"),
+]
+
+
+@pytest.mark.parametrize("kind,H,d,shape,mk", WIDE_CASES,
+                         ids=[f"{c[0]}-H{c[1]}-d{c[2]}-{c[4]}" for c in WIDE_CASES])
+def test_any_head_dim_and_many_heads(kind, H, d, shape, mk):
+    if kind == "prefill":
+        T, P = shape
+        inp = W.random_prefill(600 + H + d, T, P, H, d, 24, mask_kind=mk, w_kind="signed")
+    else:
+        R, Q, lo, hi = shape
+        width = hi + (-hi) % 8
+        inp = W.random_decode(700 + H + d, R, Q, H, d, 64, lo, hi, 24, w_kind="signed",
+                              max_seq_len=width, mask_kind=mk)
+    _full_check(inp, f"{kind} H={H} d={d} mask={mk}")
+
+
+@pytest.mark.parametrize("H,d", [(96, 256), (100, 72), (40, 200)])
+def test_integer_inputs_bit_exact_wide(H, d):
+    """Exact-arithmetic inputs at padded head dimensions and over several
+    head passes: every partial sum is representable in f32, so the GPU equals
+    the oracle bit for bit whatever the summation order, on both layouts."""
+    inp = W.integer_prefill(55 + H + d, 11, 301, H, d, 30, mask_kind="random")
+    g = gpu_score(inp).cpu().numpy()
+    o = oracle.score_inputs(inp)
+    assert np.array_equal(g.astype(np.float64), o)
+    paged = W.paged_from_prefill(dataclasses.replace(inp, mask=None), 16)
+    gp = gpu_score(paged).cpu().numpy()
+    assert np.array_equal(gp.astype(np.float64), oracle.score_inputs(paged))
+
+
 def test_rows_with_nothing_visible():
     """Degenerate rows through every entry point: prefill rows hidden by a
     zero visible prefix or by an all -inf mask row, decode requests of length
