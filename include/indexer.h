@@ -180,6 +180,29 @@ indexer_status indexer_topk(
     void *stream);
 
 /*
+ * indexer_topk_blocks -- indexer_topk with block ranking (vLLM PR #45743,
+ * "Key source snippets": the decode index-score kernel takes init_blocks and
+ * local_blocks, and "decode only needs block ordering": each pooled key
+ * stands for a block of the cache, and the selection is an ordering of
+ * blocks).  The pages do not spell the two arguments out; the reading here:
+ * of each row's candidates (s < row_len[t], or every column), the first
+ * init_blocks and the last local_blocks are always selected, when selectable
+ * (a -inf or NaN score is never selected), ahead of every other key and
+ * among themselves by key index; the remaining k_top slots go to the other
+ * candidates by score descending, ties to the lower index.  If more keys are
+ * forced than k_top, the lowest-indexed are kept.  val holds the stored
+ * scores of the selected keys.  init_blocks = local_blocks = 0 is
+ * indexer_topk.  EINVAL for a negative init_blocks or local_blocks; other
+ * arguments and errors as in indexer_topk.
+ */
+indexer_status indexer_topk_blocks(
+    const float *score, int64_t score_stride_t, int32_t n_rows, int32_t n_cols,
+    const int32_t *row_len, int32_t init_blocks, int32_t local_blocks,
+    int32_t k_top, int32_t *idx, float *val, int64_t out_stride,
+    void *workspace, size_t workspace_bytes,
+    void *stream);
+
+/*
  * indexer_score_topk_fused_prefill -- indexer_score_prefill followed by
  * indexer_topk, with the score rows kept in the caller's workspace instead of
  * a caller-visible buffer.  Arguments as in the two calls; vis_len (when
@@ -214,6 +237,30 @@ indexer_status indexer_score_topk_fused_decode(
     const float *w,
     const void *mask, int64_t mask_stride_t,
     int32_t n_heads, int32_t head_dim,
+    int32_t k_top, int32_t *idx, float *val, int64_t out_stride,
+    void *workspace, size_t workspace_bytes,
+    void *stream);
+
+/*
+ * indexer_score_topk_fused_decode_blocks -- indexer_score_topk_fused_decode
+ * with block ranking (the decode index-score kernel of vLLM PR #45743 with its
+ * init_blocks and local_blocks arguments): the selection of
+ * indexer_topk_blocks over each row's visible keys (query j of request r sees
+ * s < seq_lens[r] - query_len + 1 + j), so a row's last local_blocks visible
+ * keys and its first init_blocks keys are always selected (when not masked).
+ * Same workspace as indexer_score_topk_fused_decode; EINVAL for a negative
+ * init_blocks or local_blocks.
+ */
+indexer_status indexer_score_topk_fused_decode_blocks(
+    const void *q, int64_t q_stride_t, int64_t q_stride_h,
+    const void *k_cache, int32_t block_size, int64_t k_stride_s,
+    const int32_t *block_table, int64_t bt_stride,
+    const int32_t *seq_lens,
+    int32_t n_requests, int32_t query_len, int32_t max_seq_len,
+    const float *w,
+    const void *mask, int64_t mask_stride_t,
+    int32_t n_heads, int32_t head_dim,
+    int32_t init_blocks, int32_t local_blocks,
     int32_t k_top, int32_t *idx, float *val, int64_t out_stride,
     void *workspace, size_t workspace_bytes,
     void *stream);

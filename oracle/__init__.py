@@ -54,6 +54,10 @@ def load(path: Optional[str] = None):
     lib.oracle_topk_f64.restype = None
     lib.oracle_topk_f32.argtypes = [p, i64, i32, i32, p, i32, p, p]
     lib.oracle_topk_f32.restype = None
+    lib.oracle_topk_blocks_f32.argtypes = [p, i64, i32, i32, p, i32, i32, i32, p, p]
+    lib.oracle_topk_blocks_f32.restype = None
+    lib.oracle_topk_blocks_f64.argtypes = [p, i64, i32, i32, p, i32, i32, i32, p, p]
+    lib.oracle_topk_blocks_f64.restype = None
     lib.oracle_num_threads.argtypes = []
     lib.oracle_num_threads.restype = i32
     if path == LIB:
@@ -130,6 +134,36 @@ def topk(score: np.ndarray, k_top: int, row_len=None, lib=None) -> Tuple[np.ndar
     else:
         raise TypeError(score.dtype)
     return idx, val
+
+
+def topk_blocks(score: np.ndarray, k_top: int, init_blocks: int, local_blocks: int,
+                row_len=None, lib=None) -> Tuple[np.ndarray, np.ndarray]:
+    """Block ranking: per row, the first init_blocks and last local_blocks
+    candidates forced (by index), then the rest by score; f32 or f64 rows."""
+    lib = lib or load()
+    score = np.ascontiguousarray(score)
+    n_rows, n_cols = score.shape
+    rl = None if row_len is None else np.ascontiguousarray(row_len, dtype=np.int32)
+    idx = np.empty((n_rows, k_top), dtype=np.int32)
+    if score.dtype == np.float64:
+        val = np.empty((n_rows, k_top), dtype=np.float64)
+        lib.oracle_topk_blocks_f64(_ptr(score), n_cols, n_rows, n_cols, _ptr(rl), init_blocks,
+                                   local_blocks, k_top, _ptr(idx), _ptr(val))
+    elif score.dtype == np.float32:
+        val = np.empty((n_rows, k_top), dtype=np.float32)
+        lib.oracle_topk_blocks_f32(_ptr(score), n_cols, n_rows, n_cols, _ptr(rl), init_blocks,
+                                   local_blocks, k_top, _ptr(idx), _ptr(val))
+    else:
+        raise TypeError(score.dtype)
+    return idx, val
+
+
+def decode_row_len(seq_lens, Q, max_seq_len) -> np.ndarray:
+    """Visible keys of each paged decode row r*Q + j: seq_len - Q + 1 + j,
+    clipped to [0, max_seq_len]."""
+    sl = np.asarray(seq_lens, dtype=np.int64)
+    vis = (sl[:, None] - Q + 1 + np.arange(Q)[None, :]).reshape(-1)
+    return np.clip(vis, 0, max_seq_len).astype(np.int32)
 
 
 def score_inputs(inp, lib=None) -> np.ndarray:

@@ -32,6 +32,9 @@
  * selected and -0 ties with +0.  Rows with fewer than k_top visible keys are
  * padded with index -1 and value -inf.
  *
+ * Block ranking (oracle_topk_blocks_*) follows a reading of the vLLM decode
+ * kernel's init_blocks / local_blocks arguments, spelled out above the code.
+ *
  * Pins: every function here is checked by tests/test_oracle_pins.py against
  * a hand-derived worked example, closed forms, the pages' scale identity, the
  * "materialise then sum" scheme the pages replaced, a sign-flip identity that
@@ -297,6 +300,112 @@ void oracle_topk_f32(const float *score, int64_t score_stride, int n_rows, int n
         }
         free(vals);
         free(row);
+        free(scratch);
+    }
+}
+
+/* ---------------------- block ranking (top-k) -------------------------- */
+
+/*
+ * Block ranking: the vLLM decode index-score kernel takes init_blocks and
+ * local_blocks, and decode "only needs block ordering" (vLLM PR #45743, key
+ * source snippets).  The pages leave the two arguments undefined; the reading
+ * implemented here: of a row's n candidates, the keys s < init_blocks and the
+ * keys s >= n - local_blocks are forced -- always selected when selectable,
+ * ranked ahead of every other key, and among themselves by index ascending.
+ * The other selectable keys follow by (score descending, index ascending).
+ * The first k_top of that order are output, padded with (-1, -inf).
+ */
+typedef struct {
+    double score;
+    int32_t index;
+    int forced;
+} block_cand_t;
+
+static int block_cand_cmp(const void *a, const void *b)
+{
+    const block_cand_t *x = (const block_cand_t *)a, *y = (const block_cand_t *)b;
+    if (x->forced != y->forced)
+        return x->forced ? -1 : 1;             /* forced keys first */
+    if (!x->forced) {                          /* others by score */
+        if (x->score > y->score) return -1;
+        if (x->score < y->score) return 1;
+    }
+    return (x->index > y->index) - (x->index < y->index);
+}
+
+static void topk_blocks_row(const double *row, int n, int init_blocks, int local_blocks,
+                            int k_top, block_cand_t *scratch, int32_t *idx_out, double *val_out)
+{
+    int m = 0;
+    for (int s = 0; s < n; ++s) {
+        double v = row[s];
+        if (isnan(v) || (isinf(v) && v < 0))
+            continue;                          /* never selectable, forced or not */
+        scratch[m].score = v == 0.0 ? 0.0 : v;
+        scratch[m].index = s;
+        scratch[m].forced = s < init_blocks || (local_blocks > 0 && s >= n - local_blocks);
+        ++m;
+    }
+    qsort(scratch, (size_t)m, sizeof(block_cand_t), block_cand_cmp);
+    for (int i = 0; i < k_top; ++i) {
+        if (i < m) {
+            idx_out[i] = scratch[i].index;
+            if (val_out) val_out[i] = row[scratch[i].index];
+        } else {
+            idx_out[i] = -1;
+            if (val_out) val_out[i] = -INFINITY;
+        }
+    }
+}
+
+/*
+ * Block ranking over f32 score rows [n_rows][n_cols] (each f32 widened
+ * exactly to double).  row_len i32 [n_rows] (nullable) limits row t to its
+ * first row_len[t] columns, which are its n candidates.
+ */
+void oracle_topk_blocks_f32(const float *score, int64_t score_stride, int n_rows, int n_cols,
+                            const int32_t *row_len, int init_blocks, int local_blocks, int k_top,
+                            int32_t *idx_out, float *val_out)
+{
+#pragma omp parallel
+    {
+        block_cand_t *scratch = (block_cand_t *)malloc(sizeof(block_cand_t) * (size_t)(n_cols > 0 ? n_cols : 1));
+        double *row = (double *)malloc(sizeof(double) * (size_t)(n_cols > 0 ? n_cols : 1));
+        double *vals = (double *)malloc(sizeof(double) * (size_t)(k_top > 0 ? k_top : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int t = 0; t < n_rows; ++t) {
+            int n = n_cols;
+            if (row_len && row_len[t] < n) n = row_len[t] < 0 ? 0 : row_len[t];
+            const float *src = score + (int64_t)t * score_stride;
+            for (int s = 0; s < n; ++s) row[s] = (double)src[s];
+            topk_blocks_row(row, n, init_blocks, local_blocks, k_top, scratch,
+                            idx_out + (int64_t)t * k_top, val_out ? vals : NULL);
+            if (val_out)
+                for (int i = 0; i < k_top; ++i)
+                    val_out[(int64_t)t * k_top + i] = (float)vals[i];
+        }
+        free(vals);
+        free(row);
+        free(scratch);
+    }
+}
+
+/* The same over f64 rows (the oracle's own scores). */
+void oracle_topk_blocks_f64(const double *score, int64_t score_stride, int n_rows, int n_cols,
+                            const int32_t *row_len, int init_blocks, int local_blocks, int k_top,
+                            int32_t *idx_out, double *val_out)
+{
+#pragma omp parallel
+    {
+        block_cand_t *scratch = (block_cand_t *)malloc(sizeof(block_cand_t) * (size_t)(n_cols > 0 ? n_cols : 1));
+#pragma omp for schedule(dynamic, 1)
+        for (int t = 0; t < n_rows; ++t) {
+            int n = n_cols;
+            if (row_len && row_len[t] < n) n = row_len[t] < 0 ? 0 : row_len[t];
+            topk_blocks_row(score + (int64_t)t * score_stride, n, init_blocks, local_blocks, k_top, scratch,
+                            idx_out + (int64_t)t * k_top, val_out ? val_out + (int64_t)t * k_top : NULL);
+        }
         free(scratch);
     }
 }

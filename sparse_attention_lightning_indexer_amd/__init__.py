@@ -29,6 +29,7 @@ EXPORTS = (
     "indexer_score_prefill", "indexer_score_decode", "indexer_topk",
     "indexer_score_topk_fused_prefill", "indexer_score_topk_fused_decode",
     "indexer_workspace_bytes", "indexer_score_topk_fused_decode_noalloc",
+    "indexer_topk_blocks", "indexer_score_topk_fused_decode_blocks",
 )
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -80,6 +81,12 @@ def load_library(path: str = LIB_PATH):
                                                     i32, i32, i32, p, p, i64, i32, i32,
                                                     i32, p, p, i64, p, sz, p]
     lib.indexer_score_topk_fused_decode.restype = st
+    lib.indexer_topk_blocks.argtypes = [p, i64, i32, i32, p, i32, i32, i32, p, p, i64, p, sz, p]
+    lib.indexer_topk_blocks.restype = st
+    lib.indexer_score_topk_fused_decode_blocks.argtypes = [p, i64, i64, p, i32, i64, p, i64, p,
+                                                           i32, i32, i32, p, p, i64, i32, i32,
+                                                           i32, i32, i32, p, p, i64, p, sz, p]
+    lib.indexer_score_topk_fused_decode_blocks.restype = st
     lib.indexer_score_topk_fused_decode_noalloc.argtypes = [p, i64, i64, p, i32, i64, p, i64, p,
                                                             i32, i32, i32, p, p, i64, i32, i32,
                                                             i32, p, p, i64, p]
@@ -250,6 +257,37 @@ def topk(score, k_top: int, row_len=None, with_values: bool = True,
     return idx, val
 
 
+def topk_blocks(score, k_top: int, init_blocks: int, local_blocks: int, row_len=None,
+                with_values: bool = True, idx=None, val=None) -> Tuple:
+    """Block ranking over f32 score rows: the first init_blocks and last
+    local_blocks candidates of each row always selected (by index), then the
+    best of the rest -> (idx i32 [n_rows,k], val f32 [n_rows,k] or None)."""
+    torch = _torch()
+    lib = load_library()
+    if not score.is_cuda:
+        raise ValueError("score must be a GPU tensor")
+    dev = score.device
+    _need(score, "score", torch.float32, dev, 2)
+    if score.stride(1) != 1:
+        raise ValueError("score rows must be contiguous")
+    n_rows, n_cols = score.shape
+    if row_len is not None:
+        _need(row_len, "row_len", torch.int32, dev, 1)
+        row_len = row_len.contiguous()
+    if idx is None:
+        idx = torch.empty((n_rows, k_top), dtype=torch.int32, device=dev)
+    if with_values and val is None:
+        val = torch.empty((n_rows, k_top), dtype=torch.float32, device=dev)
+    ws_n = workspace_bytes(OP_TOPK, n_rows, n_cols, k_top)
+    ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev) if ws_n else None
+    if n_rows == 0:
+        return idx, val
+    _check(lib.indexer_topk_blocks(
+        _ptr(score), score.stride(0), n_rows, n_cols, _ptr(row_len), init_blocks, local_blocks, k_top,
+        _ptr(idx), _ptr(val), idx.stride(0), _ptr(ws), ws_n, _stream(dev)))
+    return idx, val
+
+
 def _workspace(op, n_rows, n_cols, k_top, dev, workspace):
     torch = _torch()
     need = workspace_bytes(op, n_rows, n_cols, k_top)
@@ -336,6 +374,42 @@ def score_topk_fused_decode(q, k_cache, block_table, seq_lens, query_len: int,
     return idx, val
 
 
+def score_topk_fused_decode_blocks(q, k_cache, block_table, seq_lens, query_len: int,
+                                   max_seq_len: int, w, k_top: int, init_blocks: int, local_blocks: int,
+                                   mask=None, with_values: bool = True, workspace=None, idx=None, val=None):
+    """score_topk_fused_decode with block ranking: each row's first
+    init_blocks and last local_blocks visible keys are always selected."""
+    torch = _torch()
+    lib = load_library()
+    dev = _q_checks(q, w)
+    RQ, H, d = q.shape
+    bs = _paged_checks(q, k_cache, block_table, seq_lens, dev, max_seq_len)
+    R = seq_lens.shape[0]
+    if RQ != R * query_len:
+        raise ValueError(f"q has {RQ} rows, expected n_requests*query_len = {R * query_len}")
+    if mask is not None:
+        _need(mask, "mask", torch.float16, dev, 2)
+        if mask.stride(1) != 1 or tuple(mask.shape) != (RQ, max_seq_len):
+            raise ValueError("mask must be [R*Q, max_seq_len] with contiguous rows")
+    if idx is None:
+        idx = torch.empty((RQ, k_top), dtype=torch.int32, device=dev)
+    if val is None and with_values:
+        val = torch.empty((RQ, k_top), dtype=torch.float32, device=dev)
+    for o in (idx, val):
+        if o is not None and (tuple(o.shape) != (RQ, k_top) or not o.is_contiguous()):
+            raise ValueError(f"outputs must be contiguous [{RQ}, {k_top}]")
+    if RQ == 0:
+        return idx, val
+    ws, need = _workspace(OP_FUSED_DECODE, RQ, max_seq_len, k_top, dev, workspace)
+    _check(lib.indexer_score_topk_fused_decode_blocks(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k_cache), bs, k_cache.stride(1),
+        _ptr(block_table), block_table.stride(0), _ptr(seq_lens), R, query_len,
+        max_seq_len, _ptr(w), _ptr(mask), mask.stride(0) if mask is not None else 0,
+        H, d, init_blocks, local_blocks, k_top, _ptr(idx), _ptr(val), k_top, _ptr(ws), ws.numel(),
+        _stream(dev)))
+    return idx, val
+
+
 def score_topk_fused_decode_noalloc(q, k_cache, block_table, seq_lens, query_len: int,
                                     max_seq_len: int, w, k_top: int, mask=None, idx=None, val=None):
     """score_topk_fused_decode without a workspace: the library keeps the
@@ -374,6 +448,7 @@ def score_topk_fused_decode_noalloc(q, k_cache, block_table, seq_lens, query_len
 
 __all__ = [
     "score_prefill", "score_decode", "topk", "score_topk_fused_prefill",
-    "score_topk_fused_decode", "score_topk_fused_decode_noalloc", "workspace_bytes", "load_library", "IndexerError",
+    "score_topk_fused_decode", "score_topk_fused_decode_noalloc", "score_topk_fused_decode_blocks",
+    "topk_blocks", "workspace_bytes", "load_library", "IndexerError",
     "EXPORTS", "MAX_K_TOP",
 ]

@@ -229,15 +229,25 @@ indexer_status run_score(const lidx::ScoreArgs &base, int n_heads_real, int head
     return ok();
 }
 
+// Top-k over score rows.  Candidates: s < row_len[t] when given, else the
+// visible keys of paged decode rows when seq_lens is given (keys past them
+// score -inf by definition, so reading only the visible prefix gives the
+// same result), else every column.  The first init_blocks and last
+// local_blocks candidates are always selected when selectable.
 indexer_status run_topk(const float *score, int64_t score_stride_t, int32_t n_rows, int32_t n_cols,
                         const int32_t *row_len, int32_t k_top, int32_t *idx, float *val, int64_t out_stride,
-                        void *workspace, hipStream_t stream) {
+                        void *workspace, hipStream_t stream, const int32_t *seq_lens = nullptr,
+                        int32_t q_per_req = 1, int32_t init_blocks = 0, int32_t local_blocks = 0) {
     lidx::TopkArgs t{};
     t.score = score;
     t.score_st = score_stride_t;
     t.n_rows = n_rows;
     t.n_cols = n_cols;
     t.row_len = row_len;
+    t.seq_lens = seq_lens;
+    t.q_per_req = q_per_req;
+    t.init_blocks = init_blocks;
+    t.local_blocks = local_blocks;
     t.k_top = k_top;
     t.idx = idx;
     t.val = val;
@@ -252,7 +262,7 @@ indexer_status fused_decode(const void *q, int64_t q_stride_t, int64_t q_stride_
                             const int32_t *seq_lens, int32_t n_requests, int32_t query_len, int32_t max_seq_len,
                             const float *w, const void *mask, int64_t mask_stride_t, int32_t n_heads,
                             int32_t head_dim, int32_t k_top, int32_t *idx, float *val, int64_t out_stride,
-                            void *workspace, hipStream_t s) {
+                            void *workspace, hipStream_t s, int32_t init_blocks = 0, int32_t local_blocks = 0) {
     const int32_t n_rows = n_requests * query_len;
     const int64_t row = (int64_t)round_up((size_t)max_seq_len, 4);
     float *scores = (float *)workspace;
@@ -264,7 +274,15 @@ indexer_status fused_decode(const void *q, int64_t q_stride_t, int64_t q_stride_
         indexer_status st = run_score(a, n_heads, head_dim, true, n_requests, s);
         if (st != INDEXER_OK) return st;
     }
-    return run_topk(scores, row, n_rows, max_seq_len, nullptr, k_top, idx, val, out_stride, topk_ws, s);
+    // each row's candidates are its visible keys (the rest score -inf)
+    return run_topk(scores, row, n_rows, max_seq_len, nullptr, k_top, idx, val, out_stride, topk_ws, s, seq_lens,
+                    query_len, init_blocks, local_blocks);
+}
+
+indexer_status check_blocks(int32_t init_blocks, int32_t local_blocks) {
+    if (init_blocks < 0 || local_blocks < 0)
+        return fail(INDEXER_EINVAL, "init_blocks=%d local_blocks=%d must be >= 0", init_blocks, local_blocks);
+    return INDEXER_OK;
 }
 
 // Scratch of the no-allocation fused decode: a static device array, one copy
@@ -389,6 +407,47 @@ indexer_status indexer_topk(const float *score, int64_t score_stride_t, int32_t 
     if (n_rows == 0) return ok();
     return run_topk(score, score_stride_t, n_rows, n_cols, row_len, k_top, idx, val, out_stride, workspace,
                     (hipStream_t)stream);
+}
+
+indexer_status indexer_topk_blocks(const float *score, int64_t score_stride_t, int32_t n_rows, int32_t n_cols,
+                                   const int32_t *row_len, int32_t init_blocks, int32_t local_blocks, int32_t k_top,
+                                   int32_t *idx, float *val, int64_t out_stride, void *workspace,
+                                   size_t workspace_bytes, void *stream) {
+    if (n_rows < 0 || n_cols < 0) return fail(INDEXER_EINVAL, "n_rows=%d n_cols=%d must be >= 0", n_rows, n_cols);
+    indexer_status st = check_blocks(init_blocks, local_blocks);
+    if (st != INDEXER_OK) return st;
+    if ((st = check_topk_out(k_top, idx, val, out_stride)) != INDEXER_OK) return st;
+    if (n_rows > 0 && n_cols > 0 && (st = check_score_out(score, score_stride_t, n_cols)) != INDEXER_OK) return st;
+    if (row_len && !aligned(row_len, 4)) return fail(INDEXER_EINVAL, "row_len must be 4-byte aligned");
+    const size_t need = lidx::topk_workspace_bytes(n_rows, n_cols, k_top);
+    if (need && (!workspace || workspace_bytes < need))
+        return fail(INDEXER_EWORKSPACE, "top-k needs %zu workspace bytes, got %zu", need, workspace_bytes);
+    if (n_rows == 0) return ok();
+    return run_topk(score, score_stride_t, n_rows, n_cols, row_len, k_top, idx, val, out_stride, workspace,
+                    (hipStream_t)stream, nullptr, 1, init_blocks, local_blocks);
+}
+
+indexer_status indexer_score_topk_fused_decode_blocks(
+    const void *q, int64_t q_stride_t, int64_t q_stride_h, const void *k_cache, int32_t block_size,
+    int64_t k_stride_s, const int32_t *block_table, int64_t bt_stride, const int32_t *seq_lens, int32_t n_requests,
+    int32_t query_len, int32_t max_seq_len, const float *w, const void *mask, int64_t mask_stride_t,
+    int32_t n_heads, int32_t head_dim, int32_t init_blocks, int32_t local_blocks, int32_t k_top, int32_t *idx,
+    float *val, int64_t out_stride, void *workspace, size_t workspace_bytes, void *stream) {
+    indexer_status st = check_decode(q, q_stride_t, q_stride_h, k_cache, block_size, k_stride_s, block_table,
+                                     bt_stride, seq_lens, n_requests, query_len, max_seq_len, w, mask,
+                                     mask_stride_t, n_heads, head_dim);
+    if (st != INDEXER_OK) return st;
+    if ((st = check_blocks(init_blocks, local_blocks)) != INDEXER_OK) return st;
+    if ((st = check_topk_out(k_top, idx, val, out_stride)) != INDEXER_OK) return st;
+    const int32_t n_rows = n_requests * query_len;
+    const size_t need = fused_bytes(n_rows, max_seq_len, k_top);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(INDEXER_EWORKSPACE, "fused decode needs %zu bytes of 256-byte aligned workspace, got %zu", need,
+                    workspace ? workspace_bytes : 0);
+    if (n_rows == 0) return ok();
+    return fused_decode(q, q_stride_t, q_stride_h, k_cache, block_size, k_stride_s, block_table, bt_stride,
+                        seq_lens, n_requests, query_len, max_seq_len, w, mask, mask_stride_t, n_heads, head_dim,
+                        k_top, idx, val, out_stride, workspace, (hipStream_t)stream, init_blocks, local_blocks);
 }
 
 indexer_status indexer_score_topk_fused_prefill(const void *q, int64_t q_stride_t, int64_t q_stride_h,

@@ -83,7 +83,11 @@ struct TopkArgs {
     int64_t score_st;
     int32_t n_rows;
     int32_t n_cols;
-    const int32_t *row_len;
+    const int32_t *row_len;     // candidates s < row_len[t] (nullable)
+    const int32_t *seq_lens;    // else, paged rows: s < seq_lens[t / q_per_req] - q_per_req + 1 + t % q_per_req
+    int32_t q_per_req;
+    int32_t init_blocks;        // keys s < init_blocks of a row are always selected (when selectable)
+    int32_t local_blocks;       // and so are its last local_blocks candidates
     int32_t k_top;
     int32_t *idx;
     float *val;

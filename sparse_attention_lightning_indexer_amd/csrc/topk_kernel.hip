@@ -43,10 +43,45 @@ __device__ __forceinline__ uint32_t order_key(float x) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// Block ranking (the vLLM decode kernel's init_blocks / local_blocks): the
+// first init_blocks and the last local_blocks candidates of a row are always
+// selected when selectable, ahead of every other key and among themselves by
+// index.  They take the one key no score maps to (the largest finite key is
+// that of +inf, 0xff800000), so every later step ranks them first and breaks
+// their ties by index like any other.
+constexpr uint32_t kForcedKey = 0xffffffffu;
+
+// Candidates of row t: s < row_len[t], or the row's visible keys when the
+// rows are paged decode rows, or every column.
+__device__ __forceinline__ int topk_row_len(const TopkArgs &a, int t) {
+    int n = a.n_cols;
+    if (a.row_len) {
+        n = min(max(a.row_len[t], 0), n);
+    } else if (a.seq_lens) {
+        const int r = t / a.q_per_req;
+        n = min(max(a.seq_lens[r] - a.q_per_req + 1 + (t - r * a.q_per_req), 0), n);
+    }
+    return n;
+}
+
+// The forced keys of a row of n candidates are s < f_lo and s >= f_hi.
+__device__ __forceinline__ int forced_lo(const TopkArgs &a, int n) { return min(a.init_blocks, n); }
+__device__ __forceinline__ int forced_hi(const TopkArgs &a, int n) { return a.local_blocks > 0 ? max(n - a.local_blocks, 0) : n; }
+
+// FORCED: the kernel instance that ranks blocks; the plain top-k instances
+// carry no window test.
+template <bool FORCED>
+__device__ __forceinline__ uint32_t select_key(float x, int s, int f_lo, int f_hi) {
+    const uint32_t u = order_key(x);
+    if constexpr (!FORCED) return u;
+    return (u != 0u && (s < f_lo || s >= f_hi)) ? kForcedKey : u;
+}
+
 // The score a selectable key stands for (order_key inverted).  +0 and -0
-// share a key, so a zero is read back from the row to report it as stored.
+// share a key, so a zero is read back from the row to report it as stored;
+// so is a forced key's score.
 __device__ __forceinline__ float key_value(uint32_t u, const float *row, int s) {
-    if (u == 0x80000000u) return row[s];
+    if (u == 0x80000000u || u == kForcedKey) return row[s];
     return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
 }
 
@@ -170,6 +205,7 @@ __device__ int block_exclusive_scan(int v, int *tmp, int &total) {
 // three digits, each pass re-reading the row from memory, then an
 // index-ordered compaction and a bitonic sort.  Slow but unconditional: the
 // fallback of the long-row kernel below.
+template <bool FORCED>
 __device__ void topk_row_general(const TopkArgs &a, int k_pad, unsigned char *smem) {
     uint32_t *hist = reinterpret_cast<uint32_t *>(smem);
     unsigned long long *sel = reinterpret_cast<unsigned long long *>(smem + kBins * 4);
@@ -178,11 +214,11 @@ __device__ void topk_row_general(const TopkArgs &a, int k_pad, unsigned char *sm
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int t = blockIdx.x;
     const float *row = a.score + (int64_t)t * a.score_st;
-    int n = a.n_cols;
-    if (a.row_len) n = min(max(a.row_len[t], 0), n);
+    const int n = topk_row_len(a, t);
+    const int f_lo = forced_lo(a, n), f_hi = forced_hi(a, n);
     const int k = a.k_top;
 
-    auto key_at = [&](int i) -> uint32_t { return order_key(row[i]); };
+    auto key_at = [&](int i) -> uint32_t { return select_key<FORCED>(row[i], i, f_lo, f_hi); };
 
     // ---- radix select: V = k-th largest key, `need` keys == V to take ----
     uint32_t prefix = 0, pmask = 0;
@@ -398,6 +434,7 @@ __device__ void scan_bins_desc(const uint32_t *h, uint32_t *start, int nb, int t
     __syncthreads();
 }
 
+template <bool FORCED>
 __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int k_pad) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint32_t *hist = reinterpret_cast<uint32_t *>(smem);
@@ -410,8 +447,8 @@ __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int 
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int t = blockIdx.x;
     const float *row = a.score + (int64_t)t * a.score_st;
-    int n = a.n_cols;
-    if (a.row_len) n = min(max(a.row_len[t], 0), n);
+    const int n = topk_row_len(a, t);
+    const int f_lo = forced_lo(a, n), f_hi = forced_hi(a, n);
     const int k = a.k_top;
     int32_t *const idx_out = a.idx + (int64_t)t * a.out_st;
     float *const val_out = a.val ? a.val + (int64_t)t * a.out_st : nullptr;
@@ -429,8 +466,8 @@ __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int 
     __syncthreads();
     int cnt = 0;
     uint32_t mn = 0xffffffffu, mx = 0u;
-    stream_row(row, n, [&](int, float x) {
-        const uint32_t u = order_key(x);
+    stream_row(row, n, [&](int i, float x) {
+        const uint32_t u = select_key<FORCED>(x, i, f_lo, f_hi);
         if (u) {
             ++cnt;
             mn = min(mn, u);
@@ -467,7 +504,7 @@ __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int 
     if (!all) {
         if (mn == mx) {  // every selectable key equal: index order decides
             __syncthreads();
-            topk_row_general(a, k_pad, smem);
+            topk_row_general<FORCED>(a, k_pad, smem);
             return;
         }
         scan_bins_desc(hist, nullptr, 4096, k, sc);
@@ -484,8 +521,8 @@ __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int 
             nb = 1 << width;
             for (int i = tid; i < 4096; i += kThreads) hist[i] = 0u;
             __syncthreads();
-            stream_row(row, n, [&](int, float x) {
-                const uint32_t u = order_key(x);
+            stream_row(row, n, [&](int i, float x) {
+                const uint32_t u = select_key<FORCED>(x, i, f_lo, f_hi);
                 if (u) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
             });
             __syncthreads();
@@ -494,7 +531,7 @@ __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int 
             const int cnt_b = sc[2];
             if (cnt_b > kLongCand) {
                 __syncthreads();
-                topk_row_general(a, k_pad, smem);
+                topk_row_general<FORCED>(a, k_pad, smem);
                 return;
             }
         }
@@ -502,7 +539,7 @@ __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int 
 
     // ---- 3. gather every key of a bin >= B ----------------------------------
     stream_row(row, n, [&](int i, float x) {
-        const uint32_t u = order_key(x);
+        const uint32_t u = select_key<FORCED>(x, i, f_lo, f_hi);
         if (u && (int)((u >> shift) & (nb - 1)) >= B) S[atomicAdd((uint32_t *)&sc[3], 1u)] = pack(i, u);
     });
     __syncthreads();
@@ -683,7 +720,7 @@ __device__ void threshold_bin(const uint32_t *h, int nb, int need, int *sc) {
     __syncthreads();
 }
 
-template <int THREADS, int E>
+template <int THREADS, int E, bool FORCED>
 __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_kernel(TopkArgs a, int p2) {
     constexpr int NW = THREADS / 64;
     constexpr int BITS = rows_bits(THREADS), NBINS = rows_bins(THREADS);
@@ -701,15 +738,15 @@ __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_ker
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const int t = blockIdx.x;
     const float *row = a.score + (int64_t)t * a.score_st;
-    int n = a.n_cols;
-    if (a.row_len) n = min(max(a.row_len[t], 0), n);
+    const int n = topk_row_len(a, t);
+    const int f_lo = forced_lo(a, n), f_hi = forced_hi(a, n);
     const int k = a.k_top;
 
     uint32_t key[E];
 #pragma unroll
     for (int j = 0; j < E; ++j) {
         const int i = tid + THREADS * j;
-        key[j] = i < n ? order_key(row[i]) : 0u;
+        key[j] = i < n ? select_key<FORCED>(row[i], i, f_lo, f_hi) : 0u;
     }
     for (int i = tid; i < NBINS; i += THREADS) hist0[i] = 0u;
 
@@ -1018,13 +1055,30 @@ size_t rows_lds_bytes(int p2) {
     return 8 * (size_t)rows_bins(THREADS) + 8 * (size_t)(p2 + min(p2, rows_tmp_cap(THREADS))) + 4 * (size_t)E * (THREADS / 64) + 4 * (64 + THREADS / 64) + 16;
 }
 
-template <int THREADS, int E>
-hipError_t launch_rows(const TopkArgs &a, int k_pad, hipStream_t stream) {
-    auto kern = topk_rows_kernel<THREADS, E>;
+template <int THREADS, int E, bool FORCED>
+hipError_t launch_rows_f(const TopkArgs &a, int k_pad, hipStream_t stream) {
+    auto kern = topk_rows_kernel<THREADS, E, FORCED>;
     const size_t bytes = rows_lds_bytes<THREADS, E>(k_pad);
-    hipError_t e = allow_lds<topk_rows_kernel<THREADS, E>>(bytes);
+    hipError_t e = allow_lds<topk_rows_kernel<THREADS, E, FORCED>>(bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, dim3(a.n_rows), dim3(THREADS), bytes, stream, a, k_pad);
+    return hipGetLastError();
+}
+
+bool ranks_blocks(const TopkArgs &a) { return a.init_blocks > 0 || a.local_blocks > 0; }
+
+template <int THREADS, int E>
+hipError_t launch_rows(const TopkArgs &a, int k_pad, hipStream_t stream) {
+    return ranks_blocks(a) ? launch_rows_f<THREADS, E, true>(a, k_pad, stream)
+                           : launch_rows_f<THREADS, E, false>(a, k_pad, stream);
+}
+
+template <bool FORCED>
+hipError_t launch_long(const TopkArgs &a, int k_pad, hipStream_t stream) {
+    const size_t bytes = long_lds_bytes(k_pad);
+    hipError_t e = allow_lds<topk_long_kernel<FORCED>>(bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(topk_long_kernel<FORCED>, dim3(a.n_rows), dim3(kThreads), bytes, stream, a, k_pad);
     return hipGetLastError();
 }
 
@@ -1055,11 +1109,7 @@ hipError_t launch_topk(const TopkArgs &a, void *, hipStream_t stream) {
         if (n <= 8192) return launch_rows<1024, 8>(a, k_pad, stream);
         return launch_rows<1024, 16>(a, k_pad, stream);
     }
-    const size_t bytes = long_lds_bytes(k_pad);
-    hipError_t e = allow_lds<topk_long_kernel>(bytes);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(topk_long_kernel, dim3(a.n_rows), dim3(kThreads), bytes, stream, a, k_pad);
-    return hipGetLastError();
+    return ranks_blocks(a) ? launch_long<true>(a, k_pad, stream) : launch_long<false>(a, k_pad, stream);
 }
 
 }  // namespace lidx

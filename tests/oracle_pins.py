@@ -318,4 +318,55 @@ def pin_topk_against_library_sort(lib):
                 assert np.array_equal(val[t], wv.astype(dt))
 
 
+def pin_topk_blocks_example(lib):
+    g = load_golden("topk_blocks_example.json")
+    row = golden_array(g["row"])[None, :]
+    for c in g["cases"]:
+        for dt in (np.float64, np.float32):
+            idx, val = oracle.topk_blocks(row.astype(dt), c["k"], c["init"], c["local"],
+                                          np.array([c["row_len"]], np.int32), lib=lib)
+            assert idx.tolist() == [c["idx"]], (c, dt, idx)
+            assert np.array_equal(val[0], golden_array(c["val"]).astype(dt)), (c, dt, val)
+
+
+def pin_topk_blocks_against_library_sort(lib):
+    """Block ranking equals a numpy lexsort by (not forced, -score for the
+    unforced, index) over the selectable candidates, on rows with heavy
+    ties, -inf, NaN and row lengths, for windows wider than the rows too."""
+    rng = np.random.default_rng(8)
+    n_rows, n_cols = 30, 200
+    s = rng.integers(-5, 5, size=(n_rows, n_cols)).astype(np.float64)
+    s[rng.random(s.shape) < 0.15] = -np.inf
+    s[rng.random(s.shape) < 0.03] = np.nan
+    row_len = rng.integers(0, n_cols, size=n_rows, endpoint=True).astype(np.int32)
+    for init, local, k_top in [(0, 0, 17), (3, 0, 10), (0, 5, 10), (4, 6, 8), (4, 6, 40), (250, 0, 64),
+                               (0, 300, 5), (1, 1, 200)]:
+        for dt in (np.float64, np.float32):
+            idx, val = oracle.topk_blocks(s.astype(dt), k_top, init, local, row_len, lib=lib)
+            for t in range(n_rows):
+                n = int(row_len[t])
+                row = s[t, :n]
+                ok = np.nonzero(~np.isnan(row) & ~np.isneginf(row))[0]
+                forced = (ok < init) | ((local > 0) & (ok >= n - local))
+                primary = np.where(forced, 0.0, -row[ok])   # forced keys tie on 0 and go by index
+                order = ok[np.lexsort((ok, primary, ~forced))][:k_top]
+                want = np.full(k_top, -1)
+                want[: len(order)] = order
+                assert np.array_equal(idx[t], want), (init, local, k_top, dt, t)
+                wv = np.full(k_top, -np.inf)
+                wv[: len(order)] = row[order]
+                assert np.array_equal(val[t], wv.astype(dt))
+
+
+def pin_topk_blocks_without_windows_is_topk(lib):
+    """No forced keys: block ranking is the plain top-k (pinned above)."""
+    rng = np.random.default_rng(9)
+    s = rng.standard_normal((12, 90)).astype(np.float32)
+    s[rng.random(s.shape) < 0.2] = -np.inf
+    for k_top in (1, 9, 90, 120):
+        a = oracle.topk_blocks(s, k_top, 0, 0, lib=lib)
+        b = oracle.topk(s, k_top, lib=lib)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

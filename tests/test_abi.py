@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 10, names
+    assert len(names) == 12, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(li.EXPORTS)
@@ -170,3 +170,16 @@ def test_probe_argument_checks():
     assert pl.peak_probe_read(A, 17, A, None) == 1
     lib = li.load_library()
     assert not any(hasattr(lib, n) for n in ("indexer_probe_mfma", "indexer_probe_read"))
+
+
+def test_block_ranking_argument_checks(lib):
+    """Negative window sizes are refused before anything is enqueued."""
+    st = lib.indexer_topk_blocks(A, 100, 4, 100, None, -1, 0, 8, B, None, 8, None, 0, None)
+    assert st == li.EINVAL and b"init_blocks" in lib.indexer_last_error()
+    st = lib.indexer_topk_blocks(A, 100, 4, 100, None, 0, -2, 8, B, None, 8, None, 0, None)
+    assert st == li.EINVAL
+    st = lib.indexer_topk_blocks(A, 100, 4, 100, None, 1, 2, 0, B, None, 8, None, 0, None)
+    assert st == li.EINVAL   # k_top
+    st = lib.indexer_score_topk_fused_decode_blocks(A, 64 * 128, 128, B, 64, 128, A, 2, A, 2, 1, 128, A, None, 0,
+                                                    64, 128, 3, -1, 8, B, None, 8, A, 1 << 20, None)
+    assert st == li.EINVAL and b"local_blocks" in lib.indexer_last_error()

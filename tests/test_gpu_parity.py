@@ -549,6 +549,58 @@ def test_topk_many_rows_heavy_ties():
         check_topk_exact(gi, gv, s, k, where=f"heavy ties rows={n_rows} k={k}")
 
 
+# ------------------------------------------------------------ block ranking
+
+@pytest.mark.parametrize("n_cols", [300, 5000, 16384, 40000])
+def test_topk_blocks_rows(n_cols):
+    """Block ranking on every top-k kernel (row kernels of 512 and 1024
+    threads, the streaming long-row kernel): ties, -inf, NaN, row lengths
+    and windows that cover the row, equal bit for bit to the oracle's
+    ranking of the same f32 scores."""
+    rng = np.random.default_rng(n_cols + 1)
+    for rows in (6, 600) if n_cols <= 16384 else (6,):
+        s = rng.integers(-30, 30, size=(rows, n_cols)).astype(np.float32)
+        s[rng.random(s.shape) < 0.2] = -np.inf
+        s[rng.random(s.shape) < 0.01] = np.nan
+        s[0, :] = 2.0                                   # one value everywhere
+        row_len = rng.integers(0, n_cols, size=rows, endpoint=True).astype(np.int32)
+        row_len[1] = n_cols
+        for init, local, k in [(1, 16, 64), (4, 0, 512), (0, 64, 100), (3000, 0, 2048), (2, 20000, 40)]:
+            gi, gv = li.topk_blocks(dev(s), k, init, local, dev(row_len))
+            torch.cuda.synchronize()
+            oi, ov = oracle.topk_blocks(s, k, init, local, row_len)
+            assert np.array_equal(gi.cpu().numpy(), oi), f"n_cols={n_cols} rows={rows} {init},{local},{k}"
+            assert np.array_equal(gv.cpu().numpy().view(np.uint32), ov.view(np.uint32))
+
+
+@pytest.mark.parametrize("R,Q,H,lo,hi,init,local,k_top,mk", [
+    (32, 1, 64, 1, 8192, 1, 64, 512, "none"),      # the decode shape, sink block + local window
+    (8, 4, 64, 4, 16384, 4, 256, 2048, "none"),    # spec-decode: each query row's own local window
+    (12, 2, 16, 1, 900, 2, 8, 30, "bias"),         # masked keys inside the windows are not selected
+])
+def test_fused_decode_blocks(R, Q, H, lo, hi, init, local, k_top, mk):
+    width = hi + (-hi) % 8
+    inp = W.random_decode(1400 + R + Q + H, R, Q, H, 128, 64, lo, hi, k_top, w_kind="uniform",
+                          max_seq_len=width, mask_kind=mk)
+    g = gpu_score(inp).cpu().numpy()
+    gi, gv = li.score_topk_fused_decode_blocks(dev(inp.q), dev(inp.k_cache), dev(inp.block_table),
+                                               dev(inp.seq_lens), inp.Q, inp.max_seq_len, dev(inp.w),
+                                               k_top, init, local, dev(inp.mask))
+    torch.cuda.synchronize()
+    rl = oracle.decode_row_len(inp.seq_lens, inp.Q, inp.max_seq_len)
+    oi, ov = oracle.topk_blocks(g, k_top, init, local, rl)
+    assert np.array_equal(gi.cpu().numpy(), oi)
+    assert np.array_equal(gv.cpu().numpy().view(np.uint32), ov.view(np.uint32))
+    # the forced windows are present in every row that can hold them
+    gi = gi.cpu().numpy()
+    for t in range(gi.shape[0]):
+        n = int(rl[t])
+        forced = [s for s in list(range(min(init, n))) + list(range(max(n - local, 0), n))
+                  if np.isfinite(g[t, s])]
+        if len(set(forced)) <= k_top:
+            assert set(forced) <= set(gi[t].tolist())
+
+
 # ------------------------------------------------------------ full workloads
 
 def _sampled_check(inp, rows, where):

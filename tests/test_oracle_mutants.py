@@ -50,6 +50,13 @@ MUTANTS = [
     ("decode_first_block_only", "s / block_size];", "0];"),
     ("decode_mask_dropped", "                if (mask)\n                    v += half_to_double(mask[t * mask_stride_t + s]);", ""),
     ("decode_mask_row_by_request", "mask[t * mask_stride_t + s]", "mask[(int64_t)r * mask_stride_t + s]"),
+    ("blocks_forced_last", "return x->forced ? -1 : 1;", "return x->forced ? 1 : -1;"),
+    ("blocks_forced_by_score", "if (!x->forced) {                          /* others by score */",
+     "if (1) {"),
+    ("blocks_local_window_off_by_one", "s >= n - local_blocks);", "s > n - local_blocks);"),
+    ("blocks_init_window_off_by_one", "scratch[m].forced = s < init_blocks ||", "scratch[m].forced = s <= init_blocks ||"),
+    ("blocks_forced_masked_selected", "            continue;                          /* never selectable, forced or not */",
+     "            if (!(s < init_blocks || (local_blocks > 0 && s >= n - local_blocks))) continue;"),
     ("decode_mask_inside_relu", "v += half_to_double(mask[t * mask_stride_t + s]);",
      "v = fmax(v + half_to_double(mask[t * mask_stride_t + s]), 0.0);"),
 ]
