@@ -298,6 +298,33 @@ indexer_status indexer_score_topk_fused_decode_noalloc(
     void *stream);
 
 /*
+ * indexer_pool_keys -- the pooled keys the indexer scores (llama.cpp b11372
+ * notes, "qwen4exp: compute the indexer score with the lightning indexer":
+ * the lightning indexer runs on the pooled keys).  The pages do not define
+ * the pooling; the reading here is mean pooling over consecutive windows:
+ *
+ *   k_pool[p][i] = mean of k[s][i] over s in [p*pool_size,
+ *                  min((p+1)*pool_size, n_keys)),  p < ceil(n_keys / pool_size)
+ *
+ * (a short last window averages the keys it holds).  The sum is formed
+ * exactly (f64), divided once by the window's key count (f64, correctly
+ * rounded) and rounded to the nearest f16, ties to even, so the result does
+ * not depend on the order of the sum.
+ *
+ *   k       f16 [n_keys][head_dim], row stride k_stride_s (16-byte aligned)
+ *   k_pool  f16 [ceil(n_keys/pool_size)][head_dim] output, row stride
+ *           pool_stride_s (16-byte aligned); may not overlap k
+ *
+ * head_dim a multiple of 8 in [8, 1024] and pool_size in [1, 8192] (above
+ * that an f64 sum of f16 values may round), else INDEXER_ENOTSUP (a
+ * pool_size below 1 is INDEXER_EINVAL).  n_keys = 0 enqueues nothing.
+ */
+indexer_status indexer_pool_keys(
+    const void *k, int64_t k_stride_s, int32_t n_keys, int32_t head_dim,
+    int32_t pool_size, void *k_pool, int64_t pool_stride_s,
+    void *stream);
+
+/*
  * Bytes of device workspace an operation needs (0 if none).  For the fused
  * operations n_rows/n_cols are the score rows and columns (n_tokens x n_pool,
  * or n_requests*query_len x max_seq_len).  Returns (size_t)-1 for negative

@@ -29,7 +29,7 @@ EXPORTS = (
     "indexer_score_prefill", "indexer_score_decode", "indexer_topk",
     "indexer_score_topk_fused_prefill", "indexer_score_topk_fused_decode",
     "indexer_workspace_bytes", "indexer_score_topk_fused_decode_noalloc",
-    "indexer_topk_blocks", "indexer_score_topk_fused_decode_blocks",
+    "indexer_topk_blocks", "indexer_score_topk_fused_decode_blocks", "indexer_pool_keys",
 )
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -81,6 +81,8 @@ def load_library(path: str = LIB_PATH):
                                                     i32, i32, i32, p, p, i64, i32, i32,
                                                     i32, p, p, i64, p, sz, p]
     lib.indexer_score_topk_fused_decode.restype = st
+    lib.indexer_pool_keys.argtypes = [p, i64, i32, i32, i32, p, i64, p]
+    lib.indexer_pool_keys.restype = st
     lib.indexer_topk_blocks.argtypes = [p, i64, i32, i32, p, i32, i32, i32, p, p, i64, p, sz, p]
     lib.indexer_topk_blocks.restype = st
     lib.indexer_score_topk_fused_decode_blocks.argtypes = [p, i64, i64, p, i32, i64, p, i64, p,
@@ -288,6 +290,33 @@ def topk_blocks(score, k_top: int, init_blocks: int, local_blocks: int, row_len=
     return idx, val
 
 
+def pool_keys(k, pool_size: int, out=None):
+    """Mean-pool consecutive windows of pool_size keys: f16 [n_keys, d] ->
+    f16 [ceil(n_keys / pool_size), d] (a short last window averages what it
+    holds; exact sum, one rounding of the mean to f16)."""
+    torch = _torch()
+    lib = load_library()
+    if not k.is_cuda:
+        raise ValueError("k must be a GPU tensor")
+    dev = k.device
+    _need(k, "k", torch.float16, dev, 2)
+    if k.stride(1) != 1:
+        raise ValueError("k's head_dim must be contiguous")
+    n, d = k.shape
+    if pool_size < 1:
+        raise ValueError("pool_size must be >= 1")
+    n_pool = -(-n // pool_size)
+    if out is None:
+        out = torch.empty((n_pool, d), dtype=torch.float16, device=dev)
+    _need(out, "out", torch.float16, dev, 2)
+    if tuple(out.shape) != (n_pool, d) or out.stride(1) != 1:
+        raise ValueError(f"out must be [{n_pool}, {d}] with contiguous rows")
+    if n == 0:
+        return out
+    _check(lib.indexer_pool_keys(_ptr(k), k.stride(0), n, d, pool_size, _ptr(out), out.stride(0), _stream(dev)))
+    return out
+
+
 def _workspace(op, n_rows, n_cols, k_top, dev, workspace):
     torch = _torch()
     need = workspace_bytes(op, n_rows, n_cols, k_top)
@@ -449,6 +478,6 @@ def score_topk_fused_decode_noalloc(q, k_cache, block_table, seq_lens, query_len
 __all__ = [
     "score_prefill", "score_decode", "topk", "score_topk_fused_prefill",
     "score_topk_fused_decode", "score_topk_fused_decode_noalloc", "score_topk_fused_decode_blocks",
-    "topk_blocks", "workspace_bytes", "load_library", "IndexerError",
+    "topk_blocks", "pool_keys", "workspace_bytes", "load_library", "IndexerError",
     "EXPORTS", "MAX_K_TOP",
 ]

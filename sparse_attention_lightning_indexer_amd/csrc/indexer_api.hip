@@ -351,6 +351,27 @@ const char *indexer_status_string(int status) {
 
 const char *indexer_last_error(void) { return g_last_error; }
 
+indexer_status indexer_pool_keys(const void *k, int64_t k_stride_s, int32_t n_keys, int32_t head_dim,
+                                 int32_t pool_size, void *k_pool, int64_t pool_stride_s, void *stream) {
+    if (n_keys < 0) return fail(INDEXER_EINVAL, "n_keys=%d must be >= 0", n_keys);
+    if (head_dim < 8 || head_dim > 1024 || head_dim % 8)
+        return fail(INDEXER_ENOTSUP, "head_dim=%d not supported (a multiple of 8 in 8..1024)", head_dim);
+    if (pool_size < 1 || pool_size > lidx::kMaxPool)
+        return fail(pool_size < 1 ? INDEXER_EINVAL : INDEXER_ENOTSUP, "pool_size=%d must be in 1..%d", pool_size,
+                    lidx::kMaxPool);
+    if (!k || !k_pool) return fail(INDEXER_EINVAL, "k and k_pool must not be NULL");
+    if (!aligned(k, 16) || !aligned(k_pool, 16)) return fail(INDEXER_EINVAL, "k and k_pool must be 16-byte aligned");
+    if (k_stride_s < head_dim || k_stride_s % 8)
+        return fail(INDEXER_EINVAL, "k_stride_s=%lld must be >= head_dim and a multiple of 8", (long long)k_stride_s);
+    if (pool_stride_s < head_dim || pool_stride_s % 8)
+        return fail(INDEXER_EINVAL, "pool_stride_s=%lld must be >= head_dim and a multiple of 8",
+                    (long long)pool_stride_s);
+    if (n_keys == 0) return ok();
+    return hip_status(lidx::launch_pool((const _Float16 *)k, k_stride_s, n_keys, head_dim, pool_size,
+                                        (_Float16 *)k_pool, pool_stride_s, (hipStream_t)stream),
+                      "pool kernel launch");
+}
+
 size_t indexer_workspace_bytes(int op, int32_t n_rows, int32_t n_cols, int32_t k_top) {
     if (n_rows < 0 || n_cols < 0 || k_top < 0) return (size_t)-1;
     switch (op) {

@@ -97,6 +97,13 @@ struct TopkArgs {
 size_t topk_workspace_bytes(int n_rows, int n_cols, int k_top);
 hipError_t launch_topk(const TopkArgs &a, void *workspace, hipStream_t stream);
 
+// Pooled-key producer (pool_kernel.hip): mean of each window of `pool`
+// consecutive keys, f16 out; pooled_count(n_keys, pool) rows.
+constexpr int kMaxPool = 8192;  // windows whose f64 sum of f16 values is exact
+int pooled_count(int n_keys, int pool);
+hipError_t launch_pool(const _Float16 *k, int64_t k_ss, int n_keys, int head_dim, int pool, _Float16 *out,
+                       int64_t out_ss, hipStream_t stream);
+
 // Number of compute units of the current device (cached per device).
 int device_cu_count();
 

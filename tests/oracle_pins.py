@@ -11,7 +11,7 @@ from __future__ import annotations
 import numpy as np
 
 import oracle
-from oracle import materialize
+from oracle import materialize, pooling
 import workloads as W
 from conftest import golden_array, load_golden
 
@@ -367,6 +367,75 @@ def pin_topk_blocks_without_windows_is_topk(lib):
         a = oracle.topk_blocks(s, k_top, 0, 0, lib=lib)
         b = oracle.topk(s, k_top, lib=lib)
         assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+# ------------------------------------------------------------ pooled keys
+
+def pin_pool_keys_example(lib):
+    g = load_golden("pool_keys_example.json")
+    k = golden_array(g["k"]).astype(np.float16)
+    for c in g["cases"]:
+        got = pooling.pool_keys(k, c["pool"])
+        assert np.array_equal(got.astype(np.float64), golden_array(c["pooled"])), (c["pool"], got)
+    for c in g["extra"]:
+        got = pooling.pool_keys(golden_array(c["k"]).astype(np.float16), c["pool"])
+        assert np.array_equal(got.astype(np.float64), golden_array(c["pooled"])), got
+
+
+def _nearest_f16(x):
+    """The f16 nearest a Python float (ties to the even bit pattern), by
+    search over every finite f16 with exact rational distances."""
+    from fractions import Fraction
+    bits = np.arange(0, 0x7c00, dtype=np.uint32).astype(np.uint16)   # +0 .. 65504
+    mags = bits.view(np.float16).astype(np.float64)
+    a = abs(x)
+    if a >= 65520.0:
+        return np.float16(np.inf if x > 0 else -np.inf)
+    i = int(np.searchsorted(mags, a))
+    cands = [j for j in (i - 1, i) if 0 <= j < len(mags)]
+    fa = Fraction(a)
+    best = min(cands, key=lambda j: (abs(Fraction(float(mags[j])) - fa), int(bits[j]) & 1))
+    v = np.float16(mags[best])
+    return -v if (x < 0 or (x == 0 and np.signbit(x))) else v
+
+
+def pin_pool_keys_brute_force(lib):
+    """Tiny windows of random finite f16 bit patterns (subnormals, large
+    values, both signs): every pooled element equals the f16 nearest the
+    f64 rounding of the exact rational mean, found by exhaustive search."""
+    from fractions import Fraction
+    rng = np.random.default_rng(4)
+    for trial in range(6):
+        n, d, pool = int(rng.integers(1, 10)), 3, int(rng.integers(1, 5))
+        raw = rng.integers(0, 0x10000, size=(n, d)).astype(np.uint16)
+        raw[(raw & 0x7c00) == 0x7c00] &= 0x3fff          # no inf / NaN
+        k = raw.view(np.float16)
+        got = pooling.pool_keys(k, pool)
+        for p in range(got.shape[0]):
+            rows = k[p * pool: min((p + 1) * pool, n)]
+            for i in range(d):
+                exact = sum(Fraction(float(v)) for v in rows[:, i]) / rows.shape[0]
+                want = _nearest_f16(float(exact))
+                assert got[p, i].view(np.uint16) == want.view(np.uint16) or (got[p, i] == 0 and want == 0), \
+                    (trial, p, i, got[p, i], want)
+
+
+def pin_pool_keys_properties(lib):
+    """Windows of one key are the keys; one window over every key is the
+    column mean; equal keys pool to themselves; reordering keys inside a
+    window changes nothing; doubling normal-range keys doubles the result."""
+    rng = np.random.default_rng(6)
+    k = rng.standard_normal((37, 16)).astype(np.float16)
+    assert np.array_equal(pooling.pool_keys(k, 1), k)
+    whole = pooling.pool_keys(k, 64)
+    assert whole.shape == (1, 16)
+    assert np.array_equal(whole[0], (k.astype(np.float64).sum(0) / 37).astype(np.float16))
+    c = np.full((10, 8), np.float16(0.3), np.float16)
+    assert np.array_equal(pooling.pool_keys(c, 3), np.full((4, 8), np.float16(0.3), np.float16))
+    perm = np.concatenate([rng.permutation(np.arange(w, min(w + 5, 37))) for w in range(0, 37, 5)])
+    assert np.array_equal(pooling.pool_keys(k[perm], 5), pooling.pool_keys(k, 5))
+    big = (rng.uniform(1, 2, size=(20, 8)) * np.where(rng.random((20, 8)) < 0.5, -1, 1)).astype(np.float16)
+    assert np.array_equal(pooling.pool_keys(big * np.float16(2), 3), pooling.pool_keys(big, 3) * np.float16(2))
 
 
 ALL_PINS = [v for k, v in sorted(globals().items()) if k.startswith("pin_")]

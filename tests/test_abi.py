@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(li.EXPORTS)
@@ -183,3 +183,21 @@ def test_block_ranking_argument_checks(lib):
     st = lib.indexer_score_topk_fused_decode_blocks(A, 64 * 128, 128, B, 64, 128, A, 2, A, 2, 1, 128, A, None, 0,
                                                     64, 128, 3, -1, 8, B, None, 8, A, 1 << 20, None)
     assert st == li.EINVAL and b"local_blocks" in lib.indexer_last_error()
+
+
+@pytest.mark.parametrize("kw,status,msg", [
+    (dict(n=-1), li.EINVAL, b"n_keys"),
+    (dict(d=12, ks=16, ps=16), li.ENOTSUP, b"head_dim=12"),
+    (dict(d=2048, ks=2048, ps=2048), li.ENOTSUP, b"head_dim=2048"),
+    (dict(pool=0), li.EINVAL, b"pool_size=0"),
+    (dict(pool=8193), li.ENOTSUP, b"pool_size=8193"),
+    (dict(k=None), li.EINVAL, b"NULL"),
+    (dict(out=B + 8), li.EINVAL, b"aligned"),
+    (dict(ks=120), li.EINVAL, b"k_stride_s"),
+    (dict(ps=64), li.EINVAL, b"pool_stride_s"),
+])
+def test_pool_rejects(lib, kw, status, msg):
+    a = dict(k=A, ks=128, n=100, d=128, pool=4, out=B, ps=128)
+    a.update(kw)
+    assert lib.indexer_pool_keys(a["k"], a["ks"], a["n"], a["d"], a["pool"], a["out"], a["ps"], None) == status
+    assert msg in lib.indexer_last_error()

@@ -8,6 +8,7 @@ import pytest
 torch = pytest.importorskip("torch")
 
 import oracle
+from oracle import pooling
 import workloads as W
 
 pytestmark = pytest.mark.gpu
@@ -599,6 +600,47 @@ def test_fused_decode_blocks(R, Q, H, lo, hi, init, local, k_top, mk):
                   if np.isfinite(g[t, s])]
         if len(set(forced)) <= k_top:
             assert set(forced) <= set(gi[t].tolist())
+
+
+# ------------------------------------------------------------ pooled keys
+
+@pytest.mark.parametrize("n,d,pool,kind", [
+    (1, 8, 1, "normal"), (7, 64, 3, "normal"), (1000, 128, 4, "normal"), (4099, 128, 64, "normal"),
+    (513, 136, 7, "bits"), (2048, 256, 2, "bits"), (3000, 64, 513, "normal"), (97, 128, 100, "bits"),
+    (20000, 128, 8192, "normal"),
+])
+def test_pool_keys_bit_exact(n, d, pool, kind):
+    """Mean pooling on the GPU equals the oracle bit for bit: N(0,1) keys,
+    and keys of random finite f16 bit patterns (subnormals, values near
+    65504, both signs); full and short last windows."""
+    rng = np.random.default_rng(n + d + pool)
+    if kind == "normal":
+        k = rng.standard_normal((n, d)).astype(np.float16)
+    else:
+        raw = rng.integers(0, 0x10000, size=(n, d)).astype(np.uint16)
+        raw[(raw & 0x7c00) == 0x7c00] &= 0x3fff
+        k = raw.view(np.float16)
+    got = li.pool_keys(dev(k), pool).cpu().numpy()
+    want = pooling.pool_keys(k, pool)
+    assert np.array_equal(got.view(np.uint16), want.view(np.uint16))
+
+
+def test_pool_keys_strided_and_scored():
+    """Row strides past head_dim on both sides, and the pooled keys fed to
+    the score: pooled on the GPU then scored equals the oracle's pooled keys
+    scored by the oracle."""
+    rng = np.random.default_rng(3)
+    raw = rng.standard_normal((1200, 160)).astype(np.float16)
+    k_view = dev(raw)[:, :128]                        # row stride 160
+    out = torch.empty((300, 136), dtype=torch.float16, device=DEV)[:, :128]
+    got = li.pool_keys(k_view, 4, out=out)
+    torch.cuda.synchronize()
+    want = pooling.pool_keys(raw[:, :128], 4)
+    assert np.array_equal(got.cpu().numpy().view(np.uint16), want.view(np.uint16))
+    inp = W.random_prefill(5, 9, 300, 64, 128, 16, mask_kind="random", w_kind="uniform")
+    inp = dataclasses.replace(inp, k=want)
+    g = li.score_prefill(dev(inp.q), got.contiguous(), dev(inp.w), dev(inp.mask)).cpu().numpy()
+    check_scores(g, oracle.score_inputs(inp), denominators(inp), where="pooled keys scored")
 
 
 # ------------------------------------------------------------ full workloads

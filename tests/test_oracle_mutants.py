@@ -12,7 +12,7 @@ import oracle
 
 _RUNNER = """
 import json, sys
-sys.path[:0] = [{root!r}, {tests!r}]
+sys.path[:0] = [{pkgroot!r}, {root!r}, {tests!r}]
 import oracle
 from oracle_pins import ALL_PINS
 lib = oracle.load({so!r})
@@ -62,6 +62,38 @@ MUTANTS = [
 ]
 
 
+# (name, text in oracle/pooling.py, replacement): the Python part of the oracle
+PY_MUTANTS = [
+    ("pool_divides_by_window_size", "mean = total / window.shape[0]", "mean = total / pool"),
+    ("pool_windows_overlap", "k[p * pool: min((p + 1) * pool, n)]", "k[p * pool: min((p + 1) * pool + 1, n)]"),
+    ("pool_rounds_through_f32", "out[p] = mean.astype(np.float16)", "out[p] = mean.astype(np.float32).astype(np.float16)"),
+    ("pool_last_window_dropped", "n_pool = -(-n // pool)", "n_pool = max(n // pool, 1)"),
+]
+
+
+def _run_pins(tmp_path, so, pkgroot):
+    tests = os.path.dirname(os.path.abspath(__file__))
+    code = _RUNNER.format(pkgroot=pkgroot, root=os.path.dirname(tests), tests=tests, so=so)
+    # each mutant runs in its own process so that a planted mistake cannot
+    # disturb the test process
+    res = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    return res
+
+
+@pytest.mark.parametrize("name,old,new", PY_MUTANTS, ids=[m[0] for m in PY_MUTANTS])
+def test_pins_catch_python_mutant(name, old, new, tmp_path):
+    import shutil
+    pkg = tmp_path / "oracle"
+    shutil.copytree(os.path.dirname(oracle.SRC), pkg, ignore=shutil.ignore_patterns("*.so", "__pycache__"))
+    src = (pkg / "pooling.py").read_text()
+    assert src.count(old) >= 1, f"mutation anchor for {name} not found"
+    (pkg / "pooling.py").write_text(src.replace(old, new))
+    res = _run_pins(tmp_path, oracle.LIB, str(tmp_path))
+    assert res.returncode == 0, f"mutant {name} crashed: {res.stderr[-400:]}"
+    failed = json.loads(res.stdout.strip().splitlines()[-1])
+    assert failed, f"mutant {name} survived every pin"
+
+
 @pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
 def test_pins_catch_mutant(name, old, new, tmp_path):
     src = open(oracle.SRC).read()
@@ -72,7 +104,7 @@ def test_pins_catch_mutant(name, old, new, tmp_path):
     so = str(tmp_path / "libmutant.so")
     oracle.build(str(path), so, extra_flags=("-w",))
     tests = os.path.dirname(os.path.abspath(__file__))
-    code = _RUNNER.format(root=os.path.dirname(tests), tests=tests, so=so)
+    code = _RUNNER.format(pkgroot=os.path.dirname(tests), root=os.path.dirname(tests), tests=tests, so=so)
     # each mutant runs in its own process so that a planted mistake cannot
     # disturb the test process
     res = subprocess.run([sys.executable, "-c", code], capture_output=True,
