@@ -77,7 +77,8 @@ typedef enum {
 typedef enum {
     INDEXER_OP_TOPK = 0,
     INDEXER_OP_FUSED_PREFILL = 1,
-    INDEXER_OP_FUSED_DECODE = 2
+    INDEXER_OP_FUSED_DECODE = 2,
+    INDEXER_OP_STREAM_PREFILL = 3
 } indexer_op;
 
 /* ABI version of the loaded library (INDEXER_ABI_VERSION at build time). */
@@ -212,6 +213,37 @@ indexer_status indexer_topk_blocks(
  * n_pool, k_top) bytes, 256-byte aligned.
  */
 indexer_status indexer_score_topk_fused_prefill(
+    const void *q, int64_t q_stride_t, int64_t q_stride_h,
+    const void *k, int64_t k_stride_s,
+    const float *w,
+    const void *mask, int64_t mask_stride_t,
+    const int32_t *vis_len,
+    int32_t n_tokens, int32_t n_pool, int32_t n_heads, int32_t head_dim,
+    int32_t k_top, int32_t *idx, float *val, int64_t out_stride,
+    void *workspace, size_t workspace_bytes,
+    void *stream);
+
+/*
+ * indexer_score_topk_stream_prefill -- the result of
+ * indexer_score_topk_fused_prefill (bit for bit: the same scores, selected
+ * in the same order) without any [n_tokens][n_pool] score buffer, for long
+ * rows.  The b11372 notes cut the indexer's score memory from per-head
+ * tensors to one [n_pool, n_tokens] score; this keeps per row only candidate
+ * lists: the workgroup scoring a row group against a chunk of keys keeps,
+ * per row, the keys whose score can still be among the row's top k_top in
+ * that chunk (a bound raised by compacting the list when it fills), and a
+ * second kernel merges a row's chunk lists into its ordered top-k.
+ * Arguments as in indexer_score_topk_fused_prefill; the workspace
+ * (indexer_workspace_bytes(INDEXER_OP_STREAM_PREFILL, n_tokens, n_pool,
+ * k_top) bytes, 256-byte aligned) is
+ *   n_tokens * min(4, ceil(n_pool / 32768)) * (k_top + 2048, rounded up to
+ *   256) * 8 bytes (+ list lengths),
+ * about 128 KiB per row at k_top = 2048 however long the rows are.  The
+ * heads must fit one pass of the kernels (n_heads <= 64, or <= 32 at a
+ * head_dim above 128), else INDEXER_ENOTSUP.  A score of -0 is reported as
+ * +0 (the kernels' scores are never -0 for finite inputs).
+ */
+indexer_status indexer_score_topk_stream_prefill(
     const void *q, int64_t q_stride_t, int64_t q_stride_h,
     const void *k, int64_t k_stride_s,
     const float *w,

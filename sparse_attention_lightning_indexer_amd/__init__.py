@@ -21,7 +21,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libindexer.so")
 
 OK, EINVAL, ENOTSUP, EWORKSPACE, EHIP = range(5)
-OP_TOPK, OP_FUSED_PREFILL, OP_FUSED_DECODE = range(3)
+OP_TOPK, OP_FUSED_PREFILL, OP_FUSED_DECODE, OP_STREAM_PREFILL = range(4)
 MAX_K_TOP = 2048
 
 EXPORTS = (
@@ -30,6 +30,7 @@ EXPORTS = (
     "indexer_score_topk_fused_prefill", "indexer_score_topk_fused_decode",
     "indexer_workspace_bytes", "indexer_score_topk_fused_decode_noalloc",
     "indexer_topk_blocks", "indexer_score_topk_fused_decode_blocks", "indexer_pool_keys",
+    "indexer_score_topk_stream_prefill",
 )
 NOALLOC_SCRATCH_BYTES = 16 << 20
 
@@ -81,6 +82,10 @@ def load_library(path: str = LIB_PATH):
                                                     i32, i32, i32, p, p, i64, i32, i32,
                                                     i32, p, p, i64, p, sz, p]
     lib.indexer_score_topk_fused_decode.restype = st
+    lib.indexer_score_topk_stream_prefill.argtypes = [p, i64, i64, p, i64, p, p, i64, p,
+                                                      i32, i32, i32, i32, i32, p, p, i64,
+                                                      p, sz, p]
+    lib.indexer_score_topk_stream_prefill.restype = st
     lib.indexer_pool_keys.argtypes = [p, i64, i32, i32, i32, p, i64, p]
     lib.indexer_pool_keys.restype = st
     lib.indexer_topk_blocks.argtypes = [p, i64, i32, i32, p, i32, i32, i32, p, p, i64, p, sz, p]
@@ -365,6 +370,44 @@ def score_topk_fused_prefill(q, k, w, k_top: int, mask=None, vis_len=None,
     return idx, val
 
 
+def score_topk_stream_prefill(q, k, w, k_top: int, mask=None, vis_len=None,
+                              with_values: bool = True, workspace=None, idx=None, val=None):
+    """The result of score_topk_fused_prefill without a score buffer: per
+    row and key chunk candidate lists (about 128 KiB per row at k_top 2048),
+    merged into the ordered top-k."""
+    torch = _torch()
+    lib = load_library()
+    dev = _q_checks(q, w)
+    T, H, d = q.shape
+    _need(k, "k", torch.float16, dev, 2)
+    if k.stride(1) != 1:
+        raise ValueError("k's head_dim must be contiguous")
+    P = k.shape[0]
+    if mask is not None:
+        _need(mask, "mask", torch.float16, dev, 2)
+        if mask.stride(1) != 1 or tuple(mask.shape) != (T, P):
+            raise ValueError("mask must be [T, P] with contiguous rows")
+    if vis_len is not None:
+        _need(vis_len, "vis_len", torch.int32, dev, 1)
+        vis_len = vis_len.contiguous()
+    if idx is None:
+        idx = torch.empty((T, k_top), dtype=torch.int32, device=dev)
+    _need(idx, "idx", torch.int32, dev, 2)
+    if val is None and with_values:
+        val = torch.empty((T, k_top), dtype=torch.float32, device=dev)
+    for o in (idx, val):
+        if o is not None and (tuple(o.shape) != (T, k_top) or not o.is_contiguous()):
+            raise ValueError(f"outputs must be contiguous [{T}, {k_top}]")
+    if T == 0:
+        return idx, val
+    ws, need = _workspace(OP_STREAM_PREFILL, T, P, k_top, dev, workspace)
+    _check(lib.indexer_score_topk_stream_prefill(
+        _ptr(q), q.stride(0), q.stride(1), _ptr(k), k.stride(0), _ptr(w),
+        _ptr(mask), mask.stride(0) if mask is not None else 0, _ptr(vis_len),
+        T, P, H, d, k_top, _ptr(idx), _ptr(val), k_top, _ptr(ws), ws.numel(), _stream(dev)))
+    return idx, val
+
+
 def score_topk_fused_decode(q, k_cache, block_table, seq_lens, query_len: int,
                             max_seq_len: int, w, k_top: int, mask=None,
                             with_values: bool = True, workspace=None, idx=None, val=None):
@@ -478,6 +521,6 @@ def score_topk_fused_decode_noalloc(q, k_cache, block_table, seq_lens, query_len
 __all__ = [
     "score_prefill", "score_decode", "topk", "score_topk_fused_prefill",
     "score_topk_fused_decode", "score_topk_fused_decode_noalloc", "score_topk_fused_decode_blocks",
-    "topk_blocks", "pool_keys", "workspace_bytes", "load_library", "IndexerError",
+    "topk_blocks", "pool_keys", "score_topk_stream_prefill", "workspace_bytes", "load_library", "IndexerError",
     "EXPORTS", "MAX_K_TOP",
 ]

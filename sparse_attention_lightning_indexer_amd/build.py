@@ -19,7 +19,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libindexer.so")
-SOURCES = ["indexer_api.hip", "score_kernel.hip", "decode_kernel.hip", "topk_kernel.hip", "pool_kernel.hip"]
+SOURCES = ["indexer_api.hip", "score_kernel.hip", "decode_kernel.hip", "topk_kernel.hip", "pool_kernel.hip", "stream_topk.hip"]
 PROBE_SOURCES = ["peak_probe.hip"]
 PROBE_LIB = os.path.join(PKG, "libpeak_probe.so")
 ARCH = os.environ.get("INDEXER_OFFLOAD_ARCH", "gfx950")

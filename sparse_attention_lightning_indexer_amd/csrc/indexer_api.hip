@@ -378,6 +378,8 @@ size_t indexer_workspace_bytes(int op, int32_t n_rows, int32_t n_cols, int32_t k
         case INDEXER_OP_TOPK: return lidx::topk_workspace_bytes(n_rows, n_cols, k_top);
         case INDEXER_OP_FUSED_PREFILL:
         case INDEXER_OP_FUSED_DECODE: return fused_bytes(n_rows, n_cols, k_top);
+        case INDEXER_OP_STREAM_PREFILL:
+            return k_top > INDEXER_MAX_K_TOP ? (size_t)-1 : lidx::stream_workspace_bytes(n_rows, n_cols, k_top);
         default: return (size_t)-1;
     }
 }
@@ -469,6 +471,54 @@ indexer_status indexer_score_topk_fused_decode_blocks(
     return fused_decode(q, q_stride_t, q_stride_h, k_cache, block_size, k_stride_s, block_table, bt_stride,
                         seq_lens, n_requests, query_len, max_seq_len, w, mask, mask_stride_t, n_heads, head_dim,
                         k_top, idx, val, out_stride, workspace, (hipStream_t)stream, init_blocks, local_blocks);
+}
+
+indexer_status indexer_score_topk_stream_prefill(const void *q, int64_t q_stride_t, int64_t q_stride_h,
+                                                 const void *k, int64_t k_stride_s, const float *w,
+                                                 const void *mask, int64_t mask_stride_t, const int32_t *vis_len,
+                                                 int32_t n_tokens, int32_t n_pool, int32_t n_heads,
+                                                 int32_t head_dim, int32_t k_top, int32_t *idx, float *val,
+                                                 int64_t out_stride, void *workspace, size_t workspace_bytes,
+                                                 void *stream) {
+    indexer_status st = check_prefill(q, q_stride_t, q_stride_h, k, k_stride_s, w, mask, mask_stride_t, vis_len,
+                                      n_tokens, n_pool, n_heads, head_dim);
+    if (st != INDEXER_OK) return st;
+    if ((st = check_topk_out(k_top, idx, val, out_stride)) != INDEXER_OK) return st;
+    if (n_heads > lidx::pass_heads(lidx::compiled_dim(head_dim)))
+        return fail(INDEXER_ENOTSUP, "streaming score + top-k runs one pass over the heads: n_heads=%d exceeds %d at "
+                    "head_dim=%d", n_heads, lidx::pass_heads(lidx::compiled_dim(head_dim)), head_dim);
+    const size_t need = lidx::stream_workspace_bytes(n_tokens, n_pool, k_top);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256))
+        return fail(INDEXER_EWORKSPACE, "streaming prefill needs %zu bytes of 256-byte aligned workspace, got %zu",
+                    need, workspace ? workspace_bytes : 0);
+    if (n_tokens == 0) return ok();
+    hipStream_t s = (hipStream_t)stream;
+    lidx::ScoreArgs a = prefill_args(q, q_stride_t, q_stride_h, k, k_stride_s, w, mask, mask_stride_t, vis_len,
+                                     n_tokens, n_pool, nullptr, 0);
+    const int nc = lidx::stream_chunks(n_pool);
+    a.cand = (unsigned long long *)workspace;
+    a.cand_count = (int32_t *)((char *)workspace +
+                               round_up((size_t)n_tokens * nc * lidx::stream_cap(k_top) * 8, 256));
+    a.cand_cap = lidx::stream_cap(k_top);
+    a.k_top = k_top;
+    a.n_heads = n_heads;
+    a.head_dim = head_dim;
+    a.accumulate = 0;
+    a.add_mask = 1;
+    if (n_pool > 0) {
+        const int dpad = lidx::compiled_dim(head_dim);
+        const int hc = lidx::compiled_heads(n_heads);
+        lidx::ScorePlan p = lidx::plan_score_stream(a, hc, dpad);
+        if (a.n_chunks > nc) return fail(INDEXER_EINVAL, "internal: %d key chunks for %d lists", a.n_chunks, nc);
+        if ((int64_t)a.n_row_groups * a.n_chunks > INT32_MAX)
+            return fail(INDEXER_EINVAL, "problem too large for one launch");
+        if ((st = hip_status(lidx::launch_score_stream(a, p, hc, dpad, s), "streaming score launch")) != INDEXER_OK)
+            return st;
+    } else {
+        a.n_chunks = 0;  // no candidates: every row is padding
+    }
+    a.n_rows = n_tokens;
+    return hip_status(lidx::launch_stream_merge(a, idx, val, out_stride, s), "streaming merge launch");
 }
 
 indexer_status indexer_score_topk_fused_prefill(const void *q, int64_t q_stride_t, int64_t q_stride_h,

@@ -42,7 +42,15 @@ struct ScoreArgs {
     int32_t nc;                 // waves side by side along keys (1, 2 or 4)
     int32_t mask_vec;           // mask rows allow 16-byte loads
     int32_t score_vec;          // score rows allow 16-byte stores
+    // streaming score + top-k (no score rows): per row and key chunk a list
+    // of candidate entries (order key << 32 | ~index) and its length
+    unsigned long long *cand;   // [n_rows][n_chunks][cand_cap]
+    int32_t *cand_count;        // [n_rows][n_chunks]
+    int32_t cand_cap;
+    int32_t k_top;
 };
+
+
 
 struct ScorePlan {
     int rows_per_group;
@@ -53,6 +61,25 @@ struct ScorePlan {
     size_t lds_bytes;
     dim3 grid;
 };
+
+// Streaming score + top-k: list capacity and chunking (stream_topk.hip).
+constexpr int kStreamSlack = 2048;   // list room beyond k_top
+constexpr int kStreamCapMax = 4096;  // k_top <= 2048
+constexpr int kStreamMaxChunks = 4;
+constexpr int kStreamChunkKeys = 32768;
+inline int stream_cap(int k_top) { return (k_top + kStreamSlack + 255) / 256 * 256; }
+inline int stream_chunks(int n_cols) {
+    const int c = (n_cols + kStreamChunkKeys - 1) / kStreamChunkKeys;
+    return c < 1 ? 1 : (c > kStreamMaxChunks ? kStreamMaxChunks : c);
+}
+size_t stream_workspace_bytes(int n_rows, int n_cols, int k_top);
+// The streaming score kernel (score_kernel.hip): a.cand, a.cand_count,
+// a.cand_cap and a.k_top set; fills the launch fields like plan_score.
+ScorePlan plan_score_stream(ScoreArgs &a, int n_heads, int head_dim);
+hipError_t launch_score_stream(const ScoreArgs &a, const ScorePlan &p, int n_heads, int head_dim,
+                               hipStream_t stream);
+// The per-row merge of the candidate lists into the ordered top-k.
+hipError_t launch_stream_merge(const ScoreArgs &a, int32_t *idx, float *val, int64_t out_st, hipStream_t stream);
 
 bool score_shape_supported(int n_heads, int head_dim);
 // The smallest compiled head count (4, 8, 16, 32, 64) holding n_heads.

@@ -40,19 +40,43 @@
 
 #include "device_common.h"
 #include "internal.h"
+#include "stream_select.h"
 
 namespace lidx {
 namespace {
 
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
+constexpr int kStreamE = kStreamCapMax / kThreads;  // list entries per thread in a compaction
+
+// LDS of the streaming variant, after the key tiles: the selection scratch
+// and each row's list length and bound.
+struct StreamLds {
+    CutLds<kThreads> cut;
+    unsigned long long bound[32];
+    int cnt[32];
+    // "some list may overflow in the next tile", set by tile i in flag[i % 3],
+    // read by every wave after the barrier that starts tile i + 1 and cleared
+    // after the one that starts tile i + 2: a slot is never written while a
+    // wave may still be about to read it, so every wave sees the same value
+    int flag[3];
+};
 
 // PAD: the general instance -- fewer real heads than H (the extra heads
 // weigh 0), a head dimension below D (zero tail), or one pass of several over
 // head groups (accumulate into the stored sums; the mask on the last pass).
 // Kept separate so that the exact-shape kernel keeps its weights as plain
 // scalar loads and carries none of these checks.
-template <int H, int D, int NBW, bool PAD>
+//
+// STREAM: the scores are not stored.  Each row keeps, for this workgroup's
+// key chunk, a list of candidate entries (order key << 32 | ~index): a score
+// joins when its entry is at least the row's bound, which starts at the
+// smallest selectable entry.  Before a tile that could overflow a list, the
+// workgroup compacts it: the bound rises to one that at least k_top of the
+// list's entries reach (stream_select.h), and only those are kept.  Every
+// key of the row's top-k within the chunk stays, so the chunk lists of a row
+// hold its top-k (merged by stream_merge_kernel).
+template <int H, int D, int NBW, bool PAD, bool STREAM>
 __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
     using G = Geo<H, D>;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -85,11 +109,19 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
     };
 
     int *misc = reinterpret_cast<int *>(smem + 2 * tile_bytes);
+    StreamLds *sl = reinterpret_cast<StreamLds *>(smem + 2 * tile_bytes + 16);
 
     // ---- bound the key range: prefix lengths, then the mask ------------
     if (tid == 0) {
         misc[0] = key_lo;
         misc[1] = key_lo;
+    }
+    if constexpr (STREAM) {
+        if (tid < 32) {
+            sl->cnt[tid] = 0;
+            sl->bound[tid] = 1ull << 32;  // every selectable entry
+        }
+        if (tid < 3) sl->flag[tid] = 0;
     }
     __syncthreads();
     if (tid < row_hi - row_lo) atomicMax(&misc[0], min(row_vis(row_lo + tid), key_hi));
@@ -220,12 +252,47 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
         }
     };
 
+    // streaming: each lane's row lists and bounds
+    unsigned long long *lst[G::SLOTS];
+    unsigned long long lb[G::SLOTS];
+    const int trigger = a.cand_cap - NK;  // a list longer than this could overflow in one tile
+#pragma unroll
+    for (int j = 0; j < G::SLOTS; ++j) {
+        lst[j] = STREAM ? a.cand + ((int64_t)out_t[j] * a.n_chunks + chunk_id) * a.cand_cap : nullptr;
+        lb[j] = 0;
+    }
+    // keep the entries >= a bound that at least k_top of them reach, in place
+    auto compact = [&](int r) {
+        unsigned long long *list = a.cand + ((int64_t)(row_lo + r) * a.n_chunks + chunk_id) * a.cand_cap;
+        const int mlen = sl->cnt[r];
+        unsigned long long e[kStreamE];
+#pragma unroll
+        for (int j = 0; j < kStreamE; ++j) {
+            const int i = tid * kStreamE + j;  // a contiguous segment per thread
+            e[j] = i < mlen ? __hip_atomic_load(list + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
+        }
+        const unsigned long long bnd =
+            cut_bound<kThreads, kStreamE>([&](int j) { return e[j]; }, a.k_top, a.k_top + kStreamSlack / 2, &sl->cut);
+        int kept = 0;
+#pragma unroll
+        for (int j = 0; j < kStreamE; ++j) kept += e[j] != 0ull && e[j] >= bnd;
+        int total;
+        int off = block_excl_scan<kThreads>(kept, &sl->cut, &total);  // every segment is read by now
+#pragma unroll
+        for (int j = 0; j < kStreamE; ++j)
+            if (e[j] != 0ull && e[j] >= bnd) list[off++] = e[j];
+        if (tid == 0) {
+            sl->cnt[r] = total;
+            sl->bound[r] = bnd;
+        }
+    };
+
     // results of the previous tile, stored after the next tile's loads are
     // issued so that their write latency overlaps the following compute
     float pend[NBW][G::SLOTS];
     int pend_s = -1;
     auto flush = [&]() {
-        if (pend_s < 0) return;
+        if (STREAM || pend_s < 0) return;
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb) {
             const int s = pend_s + nb * 32;
@@ -249,6 +316,22 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
     for (int i = 0; i < n_tiles; ++i) {
         wait_vmem_all();
         __syncthreads();  // tile i is in LDS; every wave is done with tile i-1
+        if constexpr (STREAM) {
+            // every candidate of tile i-1 is stored and counted; compact the
+            // lists that the next tile could overflow
+            const int must = i > 0 ? sl->flag[(i - 1) % 3] : 0;
+            if (tid == 0 && i > 1) sl->flag[(i - 2) % 3] = 0;
+            if (must) {
+                for (int r = 0; r < rows_per_wg; ++r)
+                    if (sl->cnt[r] > trigger) {  // cnt changes only in compact() here
+                        compact(r);
+                        __syncthreads();
+                    }
+            }
+#pragma unroll
+            for (int j = 0; j < G::SLOTS; ++j)
+                lb[j] = out_t[j] < row_hi ? sl->bound[out_t[j] - row_lo] : ~0ull;
+        }
         _Float16 mcur[NBW][G::SLOTS];
 #pragma unroll
         for (int nb = 0; nb < NBW; ++nb)
@@ -310,12 +393,45 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
                     if (vis[j]) res[j] = !PAD || a.add_mask ? sum + (float)mcur[nb][j] : sum;
                 }
             }
+            if constexpr (STREAM) {
+                // candidates: a wave's two lane halves hold two rows; one
+                // LDS atomic per half claims the half's slots
 #pragma unroll
-            for (int j = 0; j < G::SLOTS; ++j) pend[nb][j] = res[j];
+                for (int j = 0; j < G::SLOTS; ++j) {
+                    const uint32_t key = vis[j] ? stream_key(res[j]) : 0u;
+                    const unsigned long long ent = stream_entry(key, s);
+                    const bool take = key != 0u && ent >= lb[j];
+                    const unsigned long long bal = __builtin_amdgcn_ballot_w64(take);
+                    if (bal != 0ull) {
+                        const uint32_t hb = kh ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+                        const int rl = out_t[j] - row_lo;
+                        int base = 0;
+                        if ((lane & 31) == 0 && hb != 0u) {
+                            const int nadd = __popc(hb);
+                            base = atomicAdd(&sl->cnt[rl], nadd);
+                            if (base + nadd > trigger) sl->flag[i % 3] = 1;
+                        }
+                        base = __shfl(base, lane & 32, 64);
+                        if (take) {
+                            const int pos = base + __popc(hb & ((1u << (lane & 31)) - 1u));
+                            if (pos < a.cand_cap) lst[j][pos] = ent;
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int j = 0; j < G::SLOTS; ++j) pend[nb][j] = res[j];
+            }
         }
         pend_s = s0 + col * NBW * 32 + m;
     }
     flush();
+    if constexpr (STREAM) {
+        wait_vmem_all();
+        __syncthreads();  // every candidate counted
+        if (tid < row_hi - row_lo) a.cand_count[(int64_t)(row_lo + tid) * a.n_chunks + chunk_id] = sl->cnt[tid];
+        return;  // no score rows to fill
+    }
 
     // ---- keys past the bound: -inf without loading anything ------------
     const int fill_lo = min(key_lo + n_tiles * NK, key_hi);
@@ -355,35 +471,36 @@ hipError_t allow_lds(size_t bytes) {
     return e;
 }
 
-template <int H, int D, int NBW, bool PAD>
+template <int H, int D, int NBW, bool PAD, bool STREAM>
 hipError_t launch_one(const ScoreArgs &a, const ScorePlan &p, hipStream_t stream) {
-    auto kern = score_kernel<H, D, NBW, PAD>;
-    hipError_t e = allow_lds<score_kernel<H, D, NBW, PAD>>(p.lds_bytes);
+    auto kern = score_kernel<H, D, NBW, PAD, STREAM>;
+    hipError_t e = allow_lds<score_kernel<H, D, NBW, PAD, STREAM>>(p.lds_bytes);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, p.grid, dim3(kThreads), p.lds_bytes, stream, a);
     return hipGetLastError();
 }
 
-template <int H, int D, bool PAD>
+template <int H, int D, bool PAD, bool STREAM>
 hipError_t launch_nbw(const ScoreArgs &a, const ScorePlan &p, hipStream_t stream) {
     if constexpr (D == 256) {
-        return p.nbw == 2 ? launch_one<H, D, 2, PAD>(a, p, stream) : launch_one<H, D, 1, PAD>(a, p, stream);
+        return p.nbw == 2 ? launch_one<H, D, 2, PAD, STREAM>(a, p, stream) : launch_one<H, D, 1, PAD, STREAM>(a, p, stream);
     } else {
-        return p.nbw == 4 ? launch_one<H, D, 4, PAD>(a, p, stream) : launch_one<H, D, 1, PAD>(a, p, stream);
+        return p.nbw == 4 ? launch_one<H, D, 4, PAD, STREAM>(a, p, stream) : launch_one<H, D, 1, PAD, STREAM>(a, p, stream);
     }
 }
 
-template <int H, int D>
+template <int H, int D, bool STREAM>
 hipError_t launch_hd(const ScoreArgs &a, const ScorePlan &p, hipStream_t stream) {
-    if (a.n_heads == H && a.head_dim == D && !a.accumulate && a.add_mask) return launch_nbw<H, D, false>(a, p, stream);
-    return launch_nbw<H, D, true>(a, p, stream);
+    if (a.n_heads == H && a.head_dim == D && !a.accumulate && a.add_mask)
+        return launch_nbw<H, D, false, STREAM>(a, p, stream);
+    return launch_nbw<H, D, true, STREAM>(a, p, stream);
 }
 
-template <int H>
+template <int H, bool STREAM>
 hipError_t launch_h(const ScoreArgs &a, const ScorePlan &p, int D, hipStream_t stream) {
-    if (D == 64) return launch_hd<H, 64>(a, p, stream);
-    if (D == 128) return launch_hd<H, 128>(a, p, stream);
-    if constexpr (H <= 32) return launch_hd<H, 256>(a, p, stream);  // a pass holds 32 heads at 256
+    if (D == 64) return launch_hd<H, 64, STREAM>(a, p, stream);
+    if (D == 128) return launch_hd<H, 128, STREAM>(a, p, stream);
+    if constexpr (H <= 32) return launch_hd<H, 256, STREAM>(a, p, stream);  // a pass holds 32 heads at 256
     return hipErrorInvalidValue;
 }
 
@@ -434,14 +551,39 @@ ScorePlan plan_score(ScoreArgs &a, int n_heads, int head_dim) {
     return p;
 }
 
-hipError_t launch_score(const ScoreArgs &a, const ScorePlan &p, int n_heads, int head_dim, hipStream_t stream) {
+template <bool STREAM>
+hipError_t launch_any(const ScoreArgs &a, const ScorePlan &p, int n_heads, int head_dim, hipStream_t stream) {
     switch (n_heads) {
-        case 4: return launch_h<4>(a, p, head_dim, stream);
-        case 8: return launch_h<8>(a, p, head_dim, stream);
-        case 16: return launch_h<16>(a, p, head_dim, stream);
-        case 32: return launch_h<32>(a, p, head_dim, stream);
-        default: return launch_h<64>(a, p, head_dim, stream);
+        case 4: return launch_h<4, STREAM>(a, p, head_dim, stream);
+        case 8: return launch_h<8, STREAM>(a, p, head_dim, stream);
+        case 16: return launch_h<16, STREAM>(a, p, head_dim, stream);
+        case 32: return launch_h<32, STREAM>(a, p, head_dim, stream);
+        default: return launch_h<64, STREAM>(a, p, head_dim, stream);
     }
+}
+
+hipError_t launch_score(const ScoreArgs &a, const ScorePlan &p, int n_heads, int head_dim, hipStream_t stream) {
+    return launch_any<false>(a, p, n_heads, head_dim, stream);
+}
+
+ScorePlan plan_score_stream(ScoreArgs &a, int n_heads, int head_dim) {
+    ScorePlan p = plan_score(a, n_heads, head_dim);
+    // key chunks: at most kStreamMaxChunks of whole tiles, fixed by the row
+    // width alone (the workspace is sized from it)
+    const int want = stream_chunks(a.n_cols);
+    const int max_tiles = (a.n_cols + p.tile_keys - 1) / p.tile_keys;
+    const int tiles_per_chunk = (max_tiles + want - 1) / want;
+    a.chunk = (tiles_per_chunk > 0 ? tiles_per_chunk : 1) * p.tile_keys;
+    a.n_chunks = (a.n_cols + a.chunk - 1) / a.chunk;
+    if (a.n_chunks < 1) a.n_chunks = 1;
+    p.lds_bytes = p.lds_bytes + sizeof(StreamLds);
+    p.grid = dim3((unsigned)(a.n_row_groups * a.n_chunks));
+    return p;
+}
+
+hipError_t launch_score_stream(const ScoreArgs &a, const ScorePlan &p, int n_heads, int head_dim,
+                               hipStream_t stream) {
+    return launch_any<true>(a, p, n_heads, head_dim, stream);
 }
 
 }  // namespace lidx

@@ -28,7 +28,7 @@ def lib():
 
 def test_exports_every_declared_symbol(lib):
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     for n in names:
         assert hasattr(lib, n), n
     assert set(names) == set(li.EXPORTS)
@@ -201,3 +201,20 @@ def test_pool_rejects(lib, kw, status, msg):
     a.update(kw)
     assert lib.indexer_pool_keys(a["k"], a["ks"], a["n"], a["d"], a["pool"], a["out"], a["ps"], None) == status
     assert msg in lib.indexer_last_error()
+
+
+def test_stream_workspace_and_checks(lib):
+    """The streaming prefill's workspace holds candidate lists, not score
+    rows: it does not grow with the row length past 4 chunks of 32768 keys;
+    more heads than one pass are refused before any launch."""
+    ws = lib.indexer_workspace_bytes(li.OP_STREAM_PREFILL, 1024, 131072, 2048)
+    assert ws == 1024 * 4 * 4096 * 8 + 1024 * 4 * 4
+    assert lib.indexer_workspace_bytes(li.OP_STREAM_PREFILL, 1024, 1 << 20, 2048) == ws
+    assert ws < lib.indexer_workspace_bytes(li.OP_FUSED_PREFILL, 1024, 131072, 2048) // 3
+    assert lib.indexer_workspace_bytes(li.OP_STREAM_PREFILL, 16, 256, 32) == 16 * 2304 * 8 + 256
+    st = lib.indexer_score_topk_stream_prefill(A, 65 * 128, 128, B, 128, A, None, 0, None, 4, 1000, 65, 128,
+                                               8, B, None, 8, A, 1 << 30, None)
+    assert st == li.ENOTSUP and b"one pass" in lib.indexer_last_error()
+    st = lib.indexer_score_topk_stream_prefill(A, 64 * 128, 128, B, 128, A, None, 0, None, 4, 1000, 64, 128,
+                                               8, B, None, 8, A, 100, None)
+    assert st == li.EWORKSPACE

@@ -602,6 +602,77 @@ def test_fused_decode_blocks(R, Q, H, lo, hi, init, local, k_top, mk):
             assert set(forced) <= set(gi[t].tolist())
 
 
+# ------------------------------------------------------------ streaming score + top-k
+
+def _stream_vs_fused(inp, where):
+    """The streaming entry point against the fused one (score rows in a
+    workspace, then the top-k kernel), bit for bit."""
+    fi, fv = gpu_fused(inp)
+    si, sv = li.score_topk_stream_prefill(dev(inp.q), dev(inp.k), dev(inp.w), inp.k_top, dev(inp.mask),
+                                          dev(inp.vis_len))
+    torch.cuda.synchronize()
+    si, sv = si.cpu().numpy(), sv.cpu().numpy()
+    if not np.array_equal(si, fi):
+        r = int(np.argwhere((si != fi).any(axis=1))[0, 0])
+        c = int(np.argwhere(si[r] != fi[r])[0, 0])
+        raise AssertionError(f"{where}: streaming index differs at row {r} pos {c}: {si[r, c-2:c+3]} vs {fi[r, c-2:c+3]}")
+    assert np.array_equal(sv.view(np.uint32), fv.view(np.uint32)), f"{where}: streaming values differ"
+    return si, sv
+
+
+@pytest.mark.parametrize("T,P,H,d,k_top,mask,wk,vis", PREFILL_CASES,
+                         ids=[f"T{c[0]}P{c[1]}H{c[2]}d{c[3]}k{c[4]}-{c[5]}-{c[6]}-{c[7]}" for c in PREFILL_CASES])
+def test_stream_random_prefill(T, P, H, d, k_top, mask, wk, vis):
+    inp = W.random_prefill(1000 + T + P + H + d, T, P, H, d, k_top, mask_kind=mask, w_kind=wk, vis_kind=vis)
+    _stream_vs_fused(inp, inp.name)
+
+
+@pytest.mark.parametrize("T,P,H,d,k_top,mask,wk", [
+    (37, 40000, 64, 128, 2048, "random", "signed"),    # two key chunks, lists compacted many times
+    (20, 100000, 64, 128, 512, "bias", "uniform"),     # four chunks
+    (9, 131072, 16, 64, 2048, "causal", "signed"),
+    (5, 70001, 48, 96, 100, "random", "signed"),       # padded heads and head dimension
+    (6, 50000, 20, 256, 1, "none", "uniform"),         # head dimension 256, k_top = 1
+    (64, 33000, 4, 64, 2000, "zero", "signed"),        # four heads: 32 rows a workgroup
+])
+def test_stream_long_rows(T, P, H, d, k_top, mask, wk):
+    inp = W.random_prefill(2000 + T + H + d, T, P, H, d, k_top, mask_kind=mask, w_kind=wk)
+    _stream_vs_fused(inp, inp.name)
+
+
+def test_stream_adversarial_rows():
+    """Rows whose every score ties (q = 0: only the index decides, so the
+    bound search resolves entries to the last digit), rows whose scores rise
+    along the keys (every key joins its list; compactions all the way), rows
+    with fewer visible keys than k_top and rows with none."""
+    T, P, H, d = 12, 70000, 4, 64
+    base = W.random_prefill(31, T, P, H, d, 2048, mask_kind="bias", w_kind="uniform")
+    ties = dataclasses.replace(base, q=np.zeros_like(base.q), mask=np.zeros((T, P), np.float16))
+    si, _ = _stream_vs_fused(ties, "all scores equal")
+    assert np.array_equal(si, np.tile(np.arange(2048, dtype=np.int32), (T, 1)))
+    q = np.zeros((T, H, d), np.float16)
+    q[:, :, 0] = 1
+    k = np.zeros((P, d), np.float16)
+    k[:, 0] = (np.arange(P) * (8.0 / P)).astype(np.float16)       # scores rise with the key
+    rising = dataclasses.replace(base, q=q, k=k, w=np.full(H, 0.125, np.float32), mask=None)
+    _stream_vs_fused(rising, "rising scores")
+    vis = np.array([0, 1, 5, 2047, 2048, 2049, 40000, 69999, 70000, 3, 0, 12345], np.int32)
+    few = dataclasses.replace(base, vis_len=vis)
+    si, _ = _stream_vs_fused(few, "short rows")
+    assert np.all(si[0] == -1) and np.all(si[10] == -1)
+
+
+@pytest.mark.parametrize("name", ["tiny", "prefill_causal", "long_chunk"])
+def test_stream_workloads(name):
+    """The streaming path on the contiguous workloads equals the fused path
+    bit for bit, and never selects a masked key."""
+    inp = getattr(W, name)()
+    si, _ = _stream_vs_fused(inp, name)
+    sel = np.where(si >= 0, si, 0)
+    picked = np.take_along_axis(inp.mask, sel, axis=1).astype(np.float32)
+    assert not np.any(np.isneginf(picked) & (si >= 0))
+
+
 # ------------------------------------------------------------ pooled keys
 
 @pytest.mark.parametrize("n,d,pool,kind", [
