@@ -34,6 +34,7 @@
 //
 // This kernel serves contiguous keys (prefill, chunked prefill); paged decode
 // has its own latency-oriented kernel (decode_kernel.hip).
+#include <float.h>
 #include <math.h>
 
 #include <atomic>
@@ -254,12 +255,17 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
 
     // streaming: each lane's row lists and bounds
     unsigned long long *lst[G::SLOTS];
-    unsigned long long lb[G::SLOTS];
+    // a row's bound L as a score and an index: entry(x, s) >= L exactly when
+    // x > lbf, or x == lbf and s <= lbs (unsigned), for x neither NaN nor
+    // -inf (those never join: every comparison below is false for them)
+    float lbf[G::SLOTS];
+    uint32_t lbs[G::SLOTS];
     const int trigger = a.cand_cap - NK;  // a list longer than this could overflow in one tile
 #pragma unroll
     for (int j = 0; j < G::SLOTS; ++j) {
         lst[j] = STREAM ? a.cand + ((int64_t)out_t[j] * a.n_chunks + chunk_id) * a.cand_cap : nullptr;
-        lb[j] = 0;
+        lbf[j] = INFINITY;
+        lbs[j] = 0u;
     }
     // keep the entries >= a bound that at least k_top of them reach, in place
     auto compact = [&](int r) {
@@ -272,7 +278,7 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
             e[j] = i < mlen ? __hip_atomic_load(list + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : 0ull;
         }
         const unsigned long long bnd =
-            cut_bound<kThreads, kStreamE>([&](int j) { return e[j]; }, a.k_top, a.k_top + kStreamSlack / 2, &sl->cut);
+            cut_bound<kThreads, kStreamE>([&](int j) { return e[j]; }, a.k_top, a.k_top + kStreamSlack / 8, &sl->cut);
         int kept = 0;
 #pragma unroll
         for (int j = 0; j < kStreamE; ++j) kept += e[j] != 0ull && e[j] >= bnd;
@@ -329,8 +335,15 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
                     }
             }
 #pragma unroll
-            for (int j = 0; j < G::SLOTS; ++j)
-                lb[j] = out_t[j] < row_hi ? sl->bound[out_t[j] - row_lo] : ~0ull;
+            for (int j = 0; j < G::SLOTS; ++j) {
+                const unsigned long long bnd = out_t[j] < row_hi ? sl->bound[out_t[j] - row_lo] : ~0ull;
+                const uint32_t bk = (uint32_t)(bnd >> 32);
+                // keys below 0x00800000 (that of -FLT_MAX) stand for no finite
+                // score: such a bound admits every finite score and +inf; a
+                // row past the group gets a NaN bound that admits nothing
+                lbf[j] = bk < 0x00800000u ? -FLT_MAX : stream_value(bk);
+                lbs[j] = bk < 0x00800000u ? 0xffffffffu : ~(uint32_t)bnd;
+            }
         }
         _Float16 mcur[NBW][G::SLOTS];
 #pragma unroll
@@ -398,9 +411,7 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
                 // LDS atomic per half claims the half's slots
 #pragma unroll
                 for (int j = 0; j < G::SLOTS; ++j) {
-                    const uint32_t key = vis[j] ? stream_key(res[j]) : 0u;
-                    const unsigned long long ent = stream_entry(key, s);
-                    const bool take = key != 0u && ent >= lb[j];
+                    const bool take = vis[j] && (res[j] > lbf[j] || (res[j] == lbf[j] && (uint32_t)s <= lbs[j]));
                     const unsigned long long bal = __builtin_amdgcn_ballot_w64(take);
                     if (bal != 0ull) {
                         const uint32_t hb = kh ? (uint32_t)(bal >> 32) : (uint32_t)bal;
@@ -414,7 +425,7 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
                         base = __shfl(base, lane & 32, 64);
                         if (take) {
                             const int pos = base + __popc(hb & ((1u << (lane & 31)) - 1u));
-                            if (pos < a.cand_cap) lst[j][pos] = ent;
+                            if (pos < a.cand_cap) lst[j][pos] = stream_entry(stream_key(res[j]), s);
                         }
                     }
                 }
