@@ -54,6 +54,9 @@ CSRC = os.path.join(ROOT, "sparse_attention_lightning_indexer_amd", "csrc")
 KERNEL_SOURCES = {
     "score": ["decode_kernel.hip", "score_kernel.hip", "device_common.h", "internal.h"],
     "topk": ["topk_kernel.hip", "device_common.h", "internal.h"],
+    "stream_score": ["score_kernel.hip", "stream_select.h", "device_common.h", "internal.h"],
+    "stream_merge": ["stream_topk.hip", "stream_select.h", "device_common.h", "internal.h"],
+    "pool": ["pool_kernel.hip", "device_common.h", "internal.h"],
 }
 TRAFFIC_MARK = "traffic-record:"
 
@@ -68,6 +71,12 @@ def source_digest(kernel: str) -> str:
 
 
 def kernel_role(name: str):
+    if "pool_keys_kernel" in name:
+        return "pool"
+    if "stream_merge" in name:
+        return "stream_merge"
+    if "score_kernel<" in name and name.replace(" ", "").split(">")[0].endswith("true"):
+        return "stream_score"  # the streaming instance (last template flag)
     if "stream_pc_kernel" in name or "decode_kernel" in name or "score_kernel" in name:
         return "score"
     if "topk" in name:
@@ -211,7 +220,10 @@ def parse():
     ap.add_argument("--steps", type=int, default=None)
     ap.add_argument("--warmup", type=int, default=None)
     ap.add_argument("--config", default="long_chunk",
-                    choices=["tiny", "decode", "spec_decode", "prefill_causal", "long_chunk"])
+                    choices=["tiny", "decode", "spec_decode", "prefill_causal", "long_chunk", "pool_keys"])
+    ap.add_argument("--path", default="fused", choices=["fused", "stream"],
+                    help="contiguous workloads: the fused entry point (score rows in a workspace, then the "
+                         "top-k) or the streaming one (candidate lists, no score rows)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -238,7 +250,11 @@ def parse():
 
 
 DEFAULT_STEPS = {"tiny": (2000, 200), "decode": (1000, 100), "spec_decode": (300, 30),
-                 "prefill_causal": (20, 3), "long_chunk": (10, 2)}
+                 "prefill_causal": (20, 3), "long_chunk": (10, 2), "pool_keys": (200, 20)}
+
+# pooled-key producer workload: the long-context keys before pooling, four
+# raw keys per pooled key (131072 pooled keys of 128 dimensions)
+POOL_RAW_KEYS, POOL_SIZE, POOL_DIM = 524288, 4, 128
 
 
 def visible_pairs_rows(inp) -> np.ndarray:
@@ -291,6 +307,10 @@ def main():
     import sparse_attention_lightning_indexer_amd as li
     import workloads as W
 
+    if args.config == "pool_keys":
+        bench_pool(args, torch, li)
+        return
+
     steps, warmup = DEFAULT_STEPS[args.config]
     steps = args.steps if args.steps is not None else steps
     warmup = args.warmup if args.warmup is not None else warmup
@@ -324,7 +344,8 @@ def main():
     score = torch.empty((n_rows, n_cols), dtype=torch.float32, device=dev)
     idx = torch.empty((n_rows, k_top), dtype=torch.int32, device=dev)
     val = torch.empty((n_rows, k_top), dtype=torch.float32, device=dev)
-    op = li.OP_FUSED_DECODE if paged else li.OP_FUSED_PREFILL
+    stream_path = args.path == "stream" and not paged
+    op = li.OP_FUSED_DECODE if paged else (li.OP_STREAM_PREFILL if stream_path else li.OP_FUSED_PREFILL)
     ws = torch.empty(li.workspace_bytes(op, n_rows, n_cols, k_top), dtype=torch.uint8, device=dev)
 
     def run_score(c):
@@ -343,6 +364,9 @@ def main():
         if paged:
             li.score_topk_fused_decode(c["q"], c["k"], shared["bt"], shared["sl"], inp.Q, inp.max_seq_len,
                                        shared["w"], k_top, c["mask"], workspace=ws, idx=idx, val=val)
+        elif stream_path:
+            li.score_topk_stream_prefill(c["q"], c["k"], shared["w"], k_top, c["mask"], shared["vis"],
+                                         workspace=ws, idx=idx, val=val)
         else:
             li.score_topk_fused_prefill(c["q"], c["k"], shared["w"], k_top, c["mask"], shared["vis"],
                                         workspace=ws, idx=idx, val=val)
@@ -444,13 +468,21 @@ def main():
         return ms
 
     kernels, kernels_median = {}, {}
-    if not args.no_kernel_split:
+    if stream_path and not args.no_kernel_split:
+        # the streaming call's two kernels run inside one entry point: timed
+        # together, and the roofline is charged on both
+        kernels["stream"], kernels_median["stream"] = avg_ms(lambda i: run_fused(copies[i % n_copies]))
+    elif not args.no_kernel_split:
         kernels["score"], kernels_median["score"] = avg_ms(lambda i: run_score(copies[i % n_copies]))
         kernels["topk"], kernels_median["topk"] = avg_ms(lambda i: run_topk())
 
     # ---- roofline of the dominant kernel --------------------------------
     out_bytes = n_rows * k_top * 8
-    if "score" not in kernels:
+    if "stream" in kernels:
+        kern, kms = "stream", kernels["stream"]
+        work = 2 * inp.H * inp.d * pairs
+        roof = dict(bound="mfma", achieved=work / (kms * 1e-3) / 1e12, peak=MFMA_F16_PEAK_TFLOPS, unit="TFLOP/s")
+    elif "score" not in kernels:
         kern, kms, work, roof = None, None, None, None
     elif kernels["score"] >= kernels["topk"]:
         kern, kms = "score", kernels["score"]
@@ -470,7 +502,7 @@ def main():
         # HBM bytes the hardware counters saw per launch of the same kernel,
         # as a rate over the same average duration (GB/s, comparable to
         # `achieved` for an HBM-bound kernel), and per launch
-        tb = stored_traffic(args.config, kern)
+        tb = None if stream_path else stored_traffic(args.config, kern)
         roof["traffic"] = None if tb is None else tb / (kms * 1e-3) / 1e9
         roof["traffic_unit"] = "GB/s"
         roof["traffic_bytes_per_launch"] = tb
@@ -507,7 +539,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.config, "rows": n_rows, "keys": n_cols, "heads": inp.H,
                    "head_dim": inp.d, "k_top": k_top, "visible_pairs": pairs,
-                   "input_copies": n_copies},
+                   "input_copies": n_copies, "path": "stream" if stream_path else "fused",
+                   "workspace_bytes": ws.numel()},
         "roofline": roof,
         "kernels_ms": kernels,
         "kernels_ms_median": kernels_median,
@@ -520,6 +553,61 @@ def main():
     if args.out:
         with open(args.out, "a") as f:
             f.write(text + "\n")
+
+
+def bench_pool(args, torch, li):
+    """The pooled-key producer alone: K launches of indexer_pool_keys over
+    rotated copies of 524288 f16 keys (128 dimensions, N(0,1)), four raw keys
+    per pooled key; throughput in raw keys per second, roofline against HBM
+    (one read of the raw keys, one write of the pooled keys)."""
+    steps, warmup = DEFAULT_STEPS["pool_keys"]
+    steps = args.steps if args.steps is not None else steps
+    warmup = args.warmup if args.warmup is not None else warmup
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    li.load_library()
+    gen = torch.Generator(device=dev).manual_seed(0)
+    raw_bytes = POOL_RAW_KEYS * POOL_DIM * 2
+    n_copies = max(1, math.ceil(2 * MALL_BYTES / raw_bytes))
+    ks = [torch.randn((POOL_RAW_KEYS, POOL_DIM), device=dev, generator=gen).half() for _ in range(n_copies)]
+    n_pool = -(-POOL_RAW_KEYS // POOL_SIZE)
+    outs = [torch.empty((n_pool, POOL_DIM), dtype=torch.float16, device=dev) for _ in range(n_copies)]
+
+    def step(i):
+        li.pool_keys(ks[i % n_copies], POOL_SIZE, out=outs[i % n_copies])
+
+    if args.calib_copy_mib > 0:  # the known-size copy for hardware byte counters
+        src = torch.ones(args.calib_copy_mib << 18, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 1.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        step(i)
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    work = raw_bytes + n_pool * POOL_DIM * 2
+    achieved = work / (ms * 1e-3) / 1e9
+    line = {
+        "metric": "pooled-key producer: raw keys/s; % of HBM roofline",
+        "value": POOL_RAW_KEYS / (ms * 1e-3), "unit": "keys/s", "n_gpus": 1, "steps": steps, "warmup": warmup,
+        "ms_per_step": ms, "timing": "eager launches", "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f64", "data": "synthetic",
+        "config": {"workload": "pool_keys", "raw_keys": POOL_RAW_KEYS, "pool_size": POOL_SIZE,
+                   "head_dim": POOL_DIM, "input_copies": n_copies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": None,
+                     "algorithmic_bytes_per_launch": work, "kernel": "pool", "kernel_ms": ms},
+    }
+    print(json.dumps(line), flush=True)
 
 
 def cpu_model() -> str:
