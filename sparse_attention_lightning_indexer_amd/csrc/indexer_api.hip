@@ -544,6 +544,7 @@ indexer_status indexer_score_topk_fused_prefill(const void *q, int64_t q_stride_
     if (n_pool > 0) {
         lidx::ScoreArgs a = prefill_args(q, q_stride_t, q_stride_h, k, k_stride_s, w, mask, mask_stride_t, vis_len,
                                          n_tokens, n_pool, scores, row);
+        a.fill_to_vis = 1;  // the top-k below reads s < vis_len[t] only
         if ((st = run_score(a, n_heads, head_dim, false, 1, s)) != INDEXER_OK) return st;
     }
     // keys at or past vis_len[t] are -inf by definition: the top-k reads

@@ -42,6 +42,7 @@ struct ScoreArgs {
     int32_t nc;                 // waves side by side along keys (1, 2 or 4)
     int32_t mask_vec;           // mask rows allow 16-byte loads
     int32_t score_vec;          // score rows allow 16-byte stores
+    int32_t fill_to_vis;        // -inf fill only below vis_len[t] (the fused top-k reads no further)
     // streaming score + top-k (no score rows): per row and key chunk a list
     // of candidate entries (order key << 32 | ~index) and its length
     unsigned long long *cand;   // [n_rows][n_chunks][cand_cap]

@@ -49,6 +49,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kWaves = 4;
 constexpr int kStreamE = kStreamCapMax / kThreads;  // list entries per thread in a compaction
+constexpr int kMiscBytes = 4 * (2 + 32);           // two bounds, then up to 32 rows' visible lengths
 
 // LDS of the streaming variant, after the key tiles: the selection scratch
 // and each row's list length and bound.
@@ -110,7 +111,7 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
     };
 
     int *misc = reinterpret_cast<int *>(smem + 2 * tile_bytes);
-    StreamLds *sl = reinterpret_cast<StreamLds *>(smem + 2 * tile_bytes + 16);
+    StreamLds *sl = reinterpret_cast<StreamLds *>(smem + 2 * tile_bytes + kMiscBytes);
 
     // ---- bound the key range: prefix lengths, then the mask ------------
     if (tid == 0) {
@@ -445,27 +446,38 @@ __global__ void __launch_bounds__(kThreads, 2) score_kernel(ScoreArgs a) {
     }
 
     // ---- keys past the bound: -inf without loading anything ------------
+    // (for the fused entry point only below each row's vis_len: its top-k
+    // reads no further, so the rest of the workspace row is left unwritten)
     const int fill_lo = min(key_lo + n_tiles * NK, key_hi);
     if (fill_lo < key_hi) {
         const int nrows = row_hi - row_lo;
         const int width = key_hi - fill_lo;
+        const bool to_vis = a.fill_to_vis && a.vis_len != nullptr;
+        if (to_vis && tid < nrows) misc[2 + tid] = row_vis(row_lo + tid);  // misc holds 32 + 2 words
+        if (to_vis) __syncthreads();
+        auto row_end = [&](int r) { return to_vis ? misc[2 + r] : key_hi; };
         if (a.score_vec && (fill_lo & 3) == 0) {
             const int w4 = width >> 2;
             const float4 ninf = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
             for (int c = tid; c < nrows * w4; c += kThreads) {
                 const int r = c / w4;
                 const int i4 = c - r * w4;
+                if (fill_lo + 4 * i4 >= row_end(r)) continue;
                 *reinterpret_cast<float4 *>(a.score + (int64_t)(row_lo + r) * a.score_st + fill_lo + 4 * i4) = ninf;
             }
             const int tail = width & 3;
             for (int c = tid; c < nrows * tail; c += kThreads) {
                 const int r = c / tail;
-                a.score[(int64_t)(row_lo + r) * a.score_st + fill_lo + 4 * w4 + (c - r * tail)] = -INFINITY;
+                const int sidx = fill_lo + 4 * w4 + (c - r * tail);
+                if (sidx >= row_end(r)) continue;
+                a.score[(int64_t)(row_lo + r) * a.score_st + sidx] = -INFINITY;
             }
         } else {
             for (int c = tid; c < nrows * width; c += kThreads) {
                 const int r = c / width;
-                a.score[(int64_t)(row_lo + r) * a.score_st + fill_lo + (c - r * width)] = -INFINITY;
+                const int sidx = fill_lo + (c - r * width);
+                if (sidx >= row_end(r)) continue;
+                a.score[(int64_t)(row_lo + r) * a.score_st + sidx] = -INFINITY;
             }
         }
     }
@@ -557,7 +569,7 @@ ScorePlan plan_score(ScoreArgs &a, int n_heads, int head_dim) {
     if (a.n_chunks < 1) a.n_chunks = 1;
 
     const size_t tile_bytes = (size_t)p.tile_keys * 2 * head_dim;
-    p.lds_bytes = 2 * tile_bytes + 16;
+    p.lds_bytes = 2 * tile_bytes + kMiscBytes;
     p.grid = dim3((unsigned)(a.n_row_groups * a.n_chunks));
     return p;
 }
