@@ -473,6 +473,69 @@ def test_graph_replays_match_eager():
             assert torch.equal(got.view(torch.int32), want.view(torch.int32)), f"replay {rep} differs"
 
 
+def test_graph_replays_of_the_other_entry_points():
+    """The streaming prefill, the block-ranking decode, the pooled-key
+    producer and the no-allocation decode captured into one HIP graph (all
+    buffers allocated beforehand): every replay, with eager calls on other
+    inputs into the same buffers between replays, equals the eager results
+    bit for bit."""
+    pre = W.random_prefill(11, 30, 40000, 64, 128, 512, mask_kind="causal", w_kind="signed")
+    other_pre = W.random_prefill(12, 30, 40000, 64, 128, 512, mask_kind="random", w_kind="uniform")
+    dec = W.random_decode(13, 6, 4, 64, 128, 64, 100, 3000, 128, max_seq_len=3000)
+    keys = np.random.default_rng(14).standard_normal((5000, 128)).astype(np.float16)
+    p_in = [dev(x) for x in (pre.q, pre.k, pre.w, pre.mask)]
+    o_in = [dev(x) for x in (other_pre.q, other_pre.k, other_pre.w, other_pre.mask)]
+    d_in = [dev(x) for x in (dec.q, dec.k_cache, dec.block_table, dec.seq_lens, dec.w)]
+    k_in = dev(keys)
+    R = dec.R * dec.Q
+    s_idx = torch.empty((pre.T, pre.k_top), dtype=torch.int32, device=DEV)
+    s_val = torch.empty((pre.T, pre.k_top), dtype=torch.float32, device=DEV)
+    s_ws = torch.empty(li.workspace_bytes(li.OP_STREAM_PREFILL, pre.T, pre.P, pre.k_top), dtype=torch.uint8, device=DEV)
+    b_idx = torch.empty((R, dec.k_top), dtype=torch.int32, device=DEV)
+    b_val = torch.empty((R, dec.k_top), dtype=torch.float32, device=DEV)
+    b_ws = torch.empty(li.workspace_bytes(li.OP_FUSED_DECODE, R, dec.max_seq_len, dec.k_top), dtype=torch.uint8, device=DEV)
+    n_idx = torch.empty((R, dec.k_top), dtype=torch.int32, device=DEV)
+    n_val = torch.empty((R, dec.k_top), dtype=torch.float32, device=DEV)
+    pooled = torch.empty((1250, 128), dtype=torch.float16, device=DEV)
+
+    def run_pre(x):
+        q, k, w, m = x
+        li.score_topk_stream_prefill(q, k, w, pre.k_top, m, workspace=s_ws, idx=s_idx, val=s_val)
+
+    def all_calls():
+        run_pre(p_in)
+        q, kc, bt, sl, w = d_in
+        li.score_topk_fused_decode_blocks(q, kc, bt, sl, dec.Q, dec.max_seq_len, w, dec.k_top, 2, 32,
+                                          workspace=b_ws, idx=b_idx, val=b_val)
+        li.pool_keys(k_in, 4, out=pooled)
+        li.score_topk_fused_decode_noalloc(q, kc, bt, sl, dec.Q, dec.max_seq_len, w, dec.k_top,
+                                           idx=n_idx, val=n_val)
+
+    outs = (s_idx, s_val, b_idx, b_val, pooled, n_idx, n_val)
+    all_calls()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    st = torch.cuda.Stream()
+    st.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(st):
+        with torch.cuda.graph(g, stream=st):
+            all_calls()
+    torch.cuda.current_stream().wait_stream(st)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        run_pre(o_in)                      # eager work on other inputs into the same buffers
+        b_idx.fill_(-5)
+        pooled.fill_(3.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(outs, ref):
+            assert torch.equal(got.view(torch.int16 if got.dtype == torch.float16 else torch.int32),
+                               want.view(torch.int16 if want.dtype == torch.float16 else torch.int32)), \
+                f"replay {rep} differs"
+
+
 def test_heads_major_query_layout():
     """q given as a [H, T, d] tensor viewed as [T, H, d] (strides T*d... ) is
     read through its strides."""
