@@ -18,8 +18,11 @@ consecutive steps do not hit the 256 MB Infinity Cache.
 Prints ONE JSON line: throughput in visible (token, key) pairs per second,
 the roofline of the dominant kernel (its average duration measured with HIP
 events on the launch stream over its own timed loop of K launches, replayed
-the same way; also the score and top-k kernels on their own), and the CPU
-oracle timed on a bounded sample of the same workload as a baseline.
+the same way; also the score and top-k kernels on their own), floors of
+the launches timed the same way (``floors_ms``: an empty kernel on each
+kernel's grid, the top-k's bytes moved without selecting, a plain read of
+the paged score's bytes), and the CPU oracle timed on a bounded sample of
+the same workload as a baseline.
 
 Workloads (``--config``):
   tiny            16 tokens x 256 keys, 4 heads of 64, top-32
@@ -237,7 +240,8 @@ def parse():
     ap.add_argument("--trace-summary", metavar="TRACE_DIR", default=None,
                     help="print the kernel table of a rocprofv3 --kernel-trace --stats run and exit")
     ap.add_argument("--no-peak-probe", action="store_true",
-                    help="skip the measured-peak probes reported beside the published peak")
+                    help="skip the measured-peak probes reported beside the published peak, and the "
+                         "launch floors (floors_ms)")
     ap.add_argument("--eager", action="store_true",
                     help="time the steps (and kernels) as Python-issued launches instead of one replay of a "
                          "captured HIP graph of them")
@@ -476,6 +480,32 @@ def main():
         kernels["score"], kernels_median["score"] = avg_ms(lambda i: run_score(copies[i % n_copies]))
         kernels["topk"], kernels_median["topk"] = avg_ms(lambda i: run_topk())
 
+    # ---- floors of the launches, timed the same way ---------------------
+    # An empty kernel on the top-k's grid (one 1024-thread workgroup per
+    # row) and, for the paged score, on the persistent kernel's (one
+    # 512-thread workgroup per compute unit); a kernel that reads each score
+    # row's visible prefix, takes one block-wide maximum and writes the k
+    # outputs (the top-k's bytes without the selection); a plain streaming
+    # read of the paged score's algorithmic bytes, over rotated buffers.
+    floors = None
+    if not args.no_peak_probe and not stream_path and not args.no_kernel_split:
+        from sparse_attention_lightning_indexer_amd import peak_probe as pp
+        floors = {"empty_topk_grid": avg_ms(lambda i: pp.empty(n_rows, 1024))[0]}
+        if n_cols <= 16384:
+            lens = torch.from_numpy(vis_rows.astype(np.int32)).to(dev)
+            pv, pi = torch.empty_like(val), torch.empty_like(idx)
+            floors["topk_bytes"] = avg_ms(lambda i: pp.rows(score, lens, k_top, pv, pi))[0]
+            del pv, pi
+        if paged:
+            cus = torch.cuda.get_device_properties(dev).multi_processor_count
+            floors["empty_score_grid"] = avg_ms(lambda i: pp.empty(cus, 512))[0]
+            nb = (score_bytes_decode(inp) + 15) // 16 * 16
+            n_rb = max(1, min(16, math.ceil(2 * MALL_BYTES / nb)))
+            bufs = [torch.zeros(nb // 4, dtype=torch.float32, device=dev) for _ in range(n_rb)]
+            sink = pp.sink_for(dev)
+            floors["score_bytes_read"] = avg_ms(lambda i: pp.read(bufs[i % n_rb], sink))[0]
+            del bufs
+
     # ---- roofline of the dominant kernel --------------------------------
     out_bytes = n_rows * k_top * 8
     if "stream" in kernels:
@@ -544,6 +574,7 @@ def main():
         "roofline": roof,
         "kernels_ms": kernels,
         "kernels_ms_median": kernels_median,
+        "floors_ms": floors,
         "wall_s": wall,
     }
     if not args.no_cpu_baseline:

@@ -19,6 +19,22 @@
 //       (device, 16-byte aligned).  Returns 1 for a bad pointer, alignment or
 //       size, 4 when the launch fails, else 0.
 //
+//   int peak_probe_empty(int32_t blocks, int32_t threads, void *stream)
+//       a kernel that does nothing, on `blocks` workgroups of `threads`
+//       (1..1024) threads: the fixed cost of one launch.  Returns 1 for bad
+//       sizes, 4 when the launch fails, else 0.
+//   int peak_probe_rows(const float *rows, int64_t stride, const int32_t *lens,
+//                       int32_t n_rows, int32_t row_len, int32_t k, float *val,
+//                       int32_t *idx, void *stream)
+//       the memory movement of a row-wise selection without the selection:
+//       one 1024-thread workgroup per row reads the row's first lens[r]
+//       floats (row_len when lens is NULL; clamped to 0..row_len), takes one
+//       block-wide maximum and writes k values (the row's first k, capped
+//       at the maximum) and k indices.  rows is [n_rows][stride] (device,
+//       stride >= row_len), val and idx are [n_rows][k] (device).  Returns 1
+//       for bad pointers or sizes (row_len and k at most 16384), 4 when the
+//       launch fails, else 0.
+//
 //  * probe_mfma_kernel: v_mfma_f32_32x32x16_f16 fed the way the score
 //    kernels feed it -- A fragments in registers, one 16-byte B fragment per
 //    lane read from XOR-swizzled LDS rows per K step, shared by four M-blocks
@@ -112,6 +128,41 @@ __global__ void __launch_bounds__(256) probe_read_kernel(const float4 *p, size_t
     if (acc.x + acc.y + acc.z + acc.w == 1.2345e-30f) sink[blockIdx.x] = acc.x;
 }
 
+__global__ void probe_empty_kernel() {}
+
+constexpr int kRowsE = 16;  // row elements per thread (rows of up to 16384)
+
+__global__ void __launch_bounds__(1024) probe_rows_kernel(const float *rows, int64_t stride, const int32_t *lens,
+                                                          int row_len, int k, float *val, int32_t *idx) {
+    __shared__ float wmax[16];
+    const int r = blockIdx.x, tid = threadIdx.x;
+    const int len = lens ? min(max(lens[r], 0), row_len) : row_len;
+    const float *p = rows + (int64_t)r * stride;
+    float x[kRowsE];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < kRowsE; ++e) {
+        const int i = tid + e * 1024;
+        x[e] = i < len ? p[i] : -INFINITY;
+        mx = fmaxf(mx, x[e]);
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((tid & 63) == 0) wmax[tid >> 6] = mx;
+    __syncthreads();
+    float bm = wmax[0];
+#pragma unroll
+    for (int w = 1; w < 16; ++w) bm = fmaxf(bm, wmax[w]);
+#pragma unroll
+    for (int e = 0; e < kRowsE; ++e) {
+        const int j = tid + e * 1024;
+        if (j < k) {
+            val[(int64_t)r * k + j] = fminf(x[e], bm);
+            idx[(int64_t)r * k + j] = j;
+        }
+    }
+}
+
 int cu_count() {
     int dev = 0, v = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 256;
@@ -139,6 +190,22 @@ int peak_probe_read(const void *buf, size_t bytes, float *sink, void *stream) {
     const int grid = 8 * lidx::cu_count();
     hipLaunchKernelGGL(lidx::probe_read_kernel, dim3(grid), dim3(256), 0, (hipStream_t)stream,
                        (const float4 *)buf, bytes / 16, sink);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int peak_probe_empty(int32_t blocks, int32_t threads, void *stream) {
+    if (blocks < 1 || threads < 1 || threads > 1024) return 1;
+    hipLaunchKernelGGL(lidx::probe_empty_kernel, dim3(blocks), dim3(threads), 0, (hipStream_t)stream);
+    return hipGetLastError() == hipSuccess ? 0 : 4;
+}
+
+int peak_probe_rows(const float *rows, int64_t stride, const int32_t *lens, int32_t n_rows, int32_t row_len,
+                    int32_t k, float *val, int32_t *idx, void *stream) {
+    if (!rows || !val || !idx || n_rows < 1 || row_len < 0 || row_len > 1024 * lidx::kRowsE || stride < row_len ||
+        k < 1 || k > 1024 * lidx::kRowsE)
+        return 1;
+    hipLaunchKernelGGL(lidx::probe_rows_kernel, dim3(n_rows), dim3(1024), 0, (hipStream_t)stream, rows, stride,
+                       lens, row_len, k, val, idx);
     return hipGetLastError() == hipSuccess ? 0 : 4;
 }
 

@@ -1,8 +1,9 @@
 """Measured peaks of the device, reported by the benchmark beside the
 published ones: an LDS-fed f16 MFMA stream on pseudo-random operands and a
-large streaming read.  Measurement helpers only, in their own library
-(``libpeak_probe.so``, built from ``csrc/peak_probe.hip``); not part of the
-indexer or its C-ABI.
+large streaming read; and floors of one launch: an empty kernel, and a
+kernel that moves a row-wise selection's bytes without selecting.
+Measurement helpers only, in their own library (``libpeak_probe.so``, built
+from ``csrc/peak_probe.hip``); not part of the indexer or its C-ABI.
 """
 from __future__ import annotations
 
@@ -30,6 +31,10 @@ def load_library(path: str = LIB_PATH):
     lib.peak_probe_mfma.restype = ctypes.c_int
     lib.peak_probe_read.argtypes = [p, sz, p, p]
     lib.peak_probe_read.restype = ctypes.c_int
+    lib.peak_probe_empty.argtypes = [i32, i32, p]
+    lib.peak_probe_empty.restype = ctypes.c_int
+    lib.peak_probe_rows.argtypes = [p, ctypes.c_int64, p, i32, i32, i32, p, p, p]
+    lib.peak_probe_rows.restype = ctypes.c_int
     if path == LIB_PATH:
         _lib = lib
     return lib
@@ -71,3 +76,36 @@ def probe_peaks(device=None, mfma_iters: int = 4000, read_bytes: int = 4 << 30, 
     del buf
     return {"mfma_f16_tflops": flops.value / (ms_m * 1e-3) / 1e12, "read_gbs": read_bytes / (ms_r * 1e-3) / 1e9,
             "mfma_ms": ms_m, "read_ms": ms_r}
+
+
+def empty(blocks: int, threads: int):
+    """Launch the empty kernel on torch's current stream."""
+    import torch
+    _ok(load_library().peak_probe_empty(blocks, threads, torch.cuda.current_stream().cuda_stream), "empty probe")
+
+
+def rows(scores, lens, k: int, val, idx):
+    """Launch the row probe on torch's current stream: scores [n_rows][n]
+    f32, lens int32 [n_rows] or None, val/idx [n_rows][k]."""
+    import torch
+    n_rows, n = scores.shape
+    assert scores.dtype == torch.float32 and scores.stride(1) == 1
+    assert val.shape == (n_rows, k) and idx.shape == (n_rows, k) and val.is_contiguous() and idx.is_contiguous()
+    assert lens is None or (lens.dtype == torch.int32 and lens.numel() == n_rows and lens.is_contiguous())
+    _ok(load_library().peak_probe_rows(scores.data_ptr(), scores.stride(0), None if lens is None else lens.data_ptr(),
+                                       n_rows, n, k, val.data_ptr(), idx.data_ptr(),
+                                       torch.cuda.current_stream().cuda_stream), "rows probe")
+
+
+def read(buf, sink):
+    """Launch the streaming-read probe over the whole of `buf` (a device
+    tensor of a multiple of 16 bytes) on torch's current stream."""
+    import torch
+    _ok(load_library().peak_probe_read(buf.data_ptr(), buf.numel() * buf.element_size(), sink.data_ptr(),
+                                       torch.cuda.current_stream().cuda_stream), "read probe")
+
+
+def sink_for(device):
+    """The device buffer the read and MFMA probes take."""
+    import torch
+    return torch.empty(load_library().peak_probe_sink_floats(), dtype=torch.float32, device=device)

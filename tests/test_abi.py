@@ -168,6 +168,14 @@ def test_probe_argument_checks():
     assert pl.peak_probe_read(None, 1 << 20, A, None) == 1
     assert pl.peak_probe_read(A + 4, 1 << 20, A, None) == 1
     assert pl.peak_probe_read(A, 17, A, None) == 1
+    assert pl.peak_probe_empty(0, 64, None) == 1
+    assert pl.peak_probe_empty(1, 1025, None) == 1
+    I = ctypes.c_void_p(16)
+    assert pl.peak_probe_rows(None, 64, None, 1, 64, 8, A, I, None) == 1
+    assert pl.peak_probe_rows(A, 32, None, 1, 64, 8, A, I, None) == 1      # stride < row_len
+    assert pl.peak_probe_rows(A, 1 << 15, None, 1, 16385, 8, A, I, None) == 1
+    assert pl.peak_probe_rows(A, 64, None, 1, 64, 16385, A, I, None) == 1
+    assert pl.peak_probe_rows(A, 64, None, 0, 64, 8, A, I, None) == 1
     lib = li.load_library()
     assert not any(hasattr(lib, n) for n in ("indexer_probe_mfma", "indexer_probe_read"))
 

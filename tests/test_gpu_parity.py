@@ -1,6 +1,7 @@
 """GPU parity: the HIP path (through the C-ABI) against the CPU oracle on the
 same seeded inputs.  See gpu_helpers.py for the comparison bars."""
 import dataclasses
+import math
 
 import numpy as np
 import pytest
@@ -842,3 +843,26 @@ def test_peak_probes_measure_something():
     r = probe_peaks(DEV, mfma_iters=200, read_bytes=256 << 20, repeats=1)
     assert 250.0 < r["mfma_f16_tflops"] < 5000.0, r
     assert 800.0 < r["read_gbs"] < 16000.0, r
+
+
+def test_floor_probes():
+    """The launch-floor probes run; the row probe writes each row's first k
+    entries of its visible prefix (-inf past it) and their indices."""
+    from sparse_attention_lightning_indexer_amd import peak_probe as pp
+    pp.empty(3, 1024)
+    g = torch.Generator().manual_seed(5)
+    sc = torch.randn((6, 3000), generator=g).to(DEV)
+    lens = torch.tensor([3000, 0, 1, 700, 2999, 64], dtype=torch.int32).to(DEV)
+    k = 1100
+    v = torch.empty((6, k), dtype=torch.float32, device=DEV)
+    i = torch.empty((6, k), dtype=torch.int32, device=DEV)
+    pp.rows(sc, lens, k, v, i)
+    torch.cuda.synchronize()
+    want = sc[:, :k].clone()
+    for r, n in enumerate(lens.tolist()):
+        want[r, n:] = -math.inf
+    assert torch.equal(v, want)
+    assert torch.equal(i.cpu(), torch.arange(k, dtype=torch.int32).expand(6, k))
+    buf = torch.zeros(1 << 20, dtype=torch.float32, device=DEV)
+    pp.read(buf, pp.sink_for(DEV))
+    torch.cuda.synchronize()
