@@ -919,30 +919,67 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
             };
 
             if constexpr (SPLIT) {
-                // the products of block nb+1 are issued before the epilogue
-                // of block nb, so the matrix cores and the vector ALUs overlap
-                f32x16 accA[MB], accB[MB];
-                {
-                    const int n = col * NBW * 32 + m;
-                    mfma_keys<H, D, MB, KS>(accA, qa, tbase + n * G::ROWB, kh, swz<D>(n));
-                }
+                // One wave per SIMD runs this, so the matrix core, the LDS
+                // and the vector ALU overlap only as far as the wave's own
+                // instruction stream interleaves them.  The tile's NBW
+                // blocks are one software pipeline of NBW * KS K steps:
+                // step st reads the B fragment of step st + PF, issues the
+                // MB products of its own fragment, and does 1/KS of the
+                // epilogue of the block before (whose products are done).
+                // Scheduling barriers keep that order.
+                constexpr int NS = NBW * KS;   // K steps of the tile
+                constexpr int PF = 3;          // fragments read ahead of their step
+                constexpr int PER = MB * 16 / KS;  // epilogue terms per step
+                static_assert((MB * 16) % KS == 0, "epilogue split");
+                f32x16 acc[2][MB];
+                half8 bq[PF + 1];
+                auto frag = [&](int st) -> half8 {
+                    const int n = (col * NBW + st / KS) * 32 + m;
+                    return *reinterpret_cast<const lds_half8 *>(tbase + n * G::ROWB +
+                                                                (((kh * KS + st % KS) ^ swz<D>(n)) << 4));
+                };
 #pragma unroll
-                for (int nb = 0; nb < NBW; ++nb) {
-                    f32x16(&cur)[MB] = (nb & 1) ? accB : accA;
-                    f32x16(&nxt)[MB] = (nb & 1) ? accA : accB;
-                    if (nb + 1 < NBW) {
-                        const int n = (col * NBW + nb + 1) * 32 + m;
-                        mfma_keys<H, D, MB, KS>(nxt, qa, tbase + n * G::ROWB, kh, swz<D>(n));
-                    }
-                    float sum = 0.0f;
+                for (int st = 0; st < PF && st < NS; ++st) bq[st] = frag(st);
+                // A block's head sum needs the other row half's partial sum
+                // (a cross-lane move through the LDS unit); it is used two
+                // steps later, so that waiting for it does not also wait for
+                // the fragment reads issued behind it.
+                constexpr int LATE = KS > 2 ? 2 : KS - 1;
+                float sum = 0.0f, done_sum = 0.0f, other = 0.0f;
+                auto store_sum = [&](int nb) {
+                    const float res[SLOTS] = {done_sum + other};
+                    store_block(res, nb);
+                };
+#pragma unroll
+                for (int st = 0; st < NS; ++st) {
+                    const int nb = st / KS, kk = st % KS;
+                    if (st + PF < NS) bq[(st + PF) % (PF + 1)] = frag(st + PF);
+                    const half8 b = bq[st % (PF + 1)];
 #pragma unroll
                     for (int mb = 0; mb < MB; ++mb)
+                        acc[nb & 1][mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(
+                            qa[mb][kk], b, kk == 0 ? f32x16{} : acc[nb & 1][mb], 0, 0, 0);
+                    if (nb > 0) {
 #pragma unroll
-                        for (int r = 0; r < 16; ++r) sum = fmaf(relu(cur[mb][r]), wv[mb][r], sum);
-                    sum += __shfl_xor(sum, 32, 64);
-                    const float res[SLOTS] = {sum};
-                    store_block(res, nb);
+                        for (int e = kk * PER; e < (kk + 1) * PER; ++e)
+                            sum = fmaf(relu(acc[(nb - 1) & 1][e / 16][e % 16]), wv[e / 16][e % 16], sum);
+                        if (nb > 1 && kk == LATE) store_sum(nb - 2);
+                        if (kk == KS - 1) {
+                            done_sum = sum;
+                            other = __shfl_xor(sum, 32, 64);
+                            sum = 0.0f;
+                        }
+                    }
+                    __builtin_amdgcn_sched_barrier(0);
                 }
+                if (NBW > 1) store_sum(NBW - 2);
+                // the last block's epilogue
+#pragma unroll
+                for (int e = 0; e < MB * 16; ++e)
+                    sum = fmaf(relu(acc[(NBW - 1) & 1][e / 16][e % 16]), wv[e / 16][e % 16], sum);
+                done_sum = sum;
+                other = __shfl_xor(sum, 32, 64);
+                store_sum(NBW - 1);
             } else {
                 // general mapping (fewer than 32 heads: one M-block of
                 // 32/heads rows).  The products of a 32-key block, K step by
