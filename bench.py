@@ -159,10 +159,13 @@ def pmc_summary(config: str, fetch_dir: str, write_dir: str, calib_mib: int) -> 
 def mfma_summary(config: str, counter_dir: str) -> str:
     """Markdown summary of a rocprofv3 --pmc run of this benchmark with the
     MFMA counters (SQ_INSTS_VALU_MFMA_MOPS_F16, SQ_VALU_MFMA_BUSY_CYCLES,
-    GRBM_GUI_ACTIVE, SQ_BUSY_CYCLES) and --kernel-trace: per kernel the mean
+    SQ_BUSY_CYCLES, GRBM_GUI_ACTIVE) and --kernel-trace: per kernel the mean
     per dispatch, the f16 MFMA flops the hardware counted (MOPS x 512), the
-    MFMA busy fraction (busy cycles over GPU-active cycles x SIMDs), and the
-    achieved shader clock (active cycles per XCD over the dispatch time)."""
+    shader clock (SQ busy cycles per shader engine over the dispatch time;
+    32 shader engines), the MFMA busy fraction (MFMA busy cycles over those
+    cycles x 1024 SIMDs), and GRBM_GUI_ACTIVE per XCD over the dispatch time
+    beside it (it reads higher than the shader clock measured inside the
+    kernels with s_memtime, so the fractions use SQ_BUSY_CYCLES)."""
     import csv
     import glob
 
@@ -178,24 +181,27 @@ def mfma_summary(config: str, counter_dir: str) -> str:
                 dur.setdefault(r["Kernel_Name"], []).append(
                     (float(r["End_Timestamp"]) - float(r["Start_Timestamp"])) * 1e-9)
     kernels = sorted({k for k, _ in vals if kernel_role(k) == "score"})
-    n_simd, n_xcd = 1024, 8
-    out = [f"| kernel | dispatches | MFMA f16 TFLOP counted | MFMA busy | active cycles/XCD | "
-           f"dispatch us | shader clock GHz | counted TFLOP/s |", "|---|---|---|---|---|---|---|---|"]
+    n_simd, n_xcd, n_se = 1024, 8, 32
+    out = [f"| kernel | dispatches | MFMA f16 TFLOP counted | dispatch us | shader clock GHz | MFMA busy | "
+           f"counted TFLOP/s | of the clock-scaled peak | GRBM clock GHz |", "|---|---|---|---|---|---|---|---|---|"]
     for k in kernels:
         def mean(c):
             v = vals.get((k, c))
             return sum(v) / len(v) if v else float("nan")
         mops = mean("SQ_INSTS_VALU_MFMA_MOPS_F16")
         busy = mean("SQ_VALU_MFMA_BUSY_CYCLES")
-        act = mean("GRBM_GUI_ACTIVE")
-        n = len(vals.get((k, "GRBM_GUI_ACTIVE"), []))
+        sq = mean("SQ_BUSY_CYCLES") / n_se
+        act = mean("GRBM_GUI_ACTIVE") / n_xcd
+        n = len(vals.get((k, "SQ_VALU_MFMA_BUSY_CYCLES"), []))
         d = dur.get(k)
         us = sum(d) / len(d) * 1e6 if d else float("nan")
         flops = mops * 512
-        cyc = act / n_xcd
+        clk = sq / (us * 1e3)
+        rate = flops / (us * 1e-6) / 1e12
+        scaled = MFMA_F16_PEAK_TFLOPS * clk / 2.4
         short = k if len(k) < 70 else k[:67] + "..."
-        out.append(f"| `{short}` | {n} | {flops / 1e12:.1f} | {busy / (cyc * n_simd):.3f} | {cyc:.4g} | "
-                   f"{us:.1f} | {cyc / (us * 1e3):.2f} | {flops / (us * 1e-6) / 1e12:.0f} |")
+        out.append(f"| `{short}` | {n} | {flops / 1e12:.3g} | {us:.1f} | {clk:.2f} | {busy / (sq * n_simd):.3f} | "
+                   f"{rate:.0f} | {rate / scaled:.3f} | {act / (us * 1e3):.2f} |")
     return "\n".join(out) + "\n"
 
 
