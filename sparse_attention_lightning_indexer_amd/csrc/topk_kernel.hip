@@ -13,15 +13,18 @@
 //    output offset; a key's position is its bin's offset plus its rank inside
 //    the bin).  Crowded bins take an adaptive 12-bit radix select, an
 //    index-ordered compaction and a bucketed or bitonic ordering.
-//  * longer rows (topk_long_kernel): the row is streamed three times to find
-//    the bin of the k-th key and gather the candidates into LDS, which are
-//    then selected and ordered the same way.
+//  * longer rows (topk_long_kernel): a sample of the row gives a bound that
+//    somewhat more than k keys should reach, and one streaming pass gathers
+//    every key at or above it into LDS; when the sample misjudges the row,
+//    up to three passes find the bin of the k-th key and gather from it.
+//    The gathered keys are then selected and ordered in LDS.
 //  * topk_row_general: the fully general streaming fallback (heavy ties).
 #include <atomic>
 
 #include "device_common.h"
 #include "indexer.h"
 #include "internal.h"
+#include "stream_select.h"
 
 #include <math.h>
 
@@ -343,8 +346,10 @@ __device__ void topk_row_general(const TopkArgs &a, int k_pad, unsigned char *sm
 
 // ---------------------------------------------------------------------------
 // Long rows (more keys than the register-resident kernel holds): one
-// workgroup per row, two per compute unit, streams the row twice (three
-// times when the first histogram is too coarse) and never orders it there.
+// workgroup per row, two per compute unit, never orders the row itself.
+// Rows of at least kSampleRowMin keys first take the sampled one-pass
+// gather (below); when it misjudges the row, or for shorter rows, the row
+// is streamed twice (three times when the first histogram is too coarse):
 //  1. count, min/max of the selectable keys and a histogram of their top 12
 //     bits, whose descending scan gives the bin B holding the k-th key;
 //  2. when B holds more than kLongCand keys, a histogram of the 12 bits just
@@ -352,9 +357,9 @@ __device__ void topk_row_general(const TopkArgs &a, int k_pad, unsigned char *sm
 //     keys over many bins);
 //  3. every key of a bin >= B is gathered into LDS (at most k plus the
 //     kLongCand keys of B).
-// The gathered set is then selected and ordered in LDS: an 11-bit
-// histogram below the set's own common prefix gives every bin its output
-// offset and the bin holding the last selected position; keys of higher bins
+// The gathered set is then selected and ordered in LDS: a histogram of up
+// to 2048 bins of the keys' distance from the set's smallest key gives every
+// bin its output offset and the bin holding the last selected position; keys of higher bins
 // go to their bin's range and are placed by their rank inside it, keys of
 // that bin are ranked among themselves.  Sets with a bin of more than
 // kMaxBucket selected keys, or more than 512 keys in the boundary bin, are
@@ -434,6 +439,161 @@ __device__ void scan_bins_desc(const uint32_t *h, uint32_t *start, int nb, int t
     __syncthreads();
 }
 
+// ---------------------------------------------------------------------------
+// One pass instead of two for long rows.  A sample of the row (32 blocks of
+// 256 consecutive keys spread evenly over it, 8 keys per thread) gives a
+// bound tau, the key of about the r-th best sampled entry, with r chosen so
+// that about 1.4 k to 1.5 k of the row's keys should reach it.  One pass then
+// counts the row's selectable keys and gathers every key >= tau.  When at
+// least k and at most the gathered set's capacity arrive, the set holds the
+// whole top k (at least k keys are >= tau, so the k-th best is >= tau) and
+// the selection goes on from it; otherwise the row takes the passes below.
+// The result is the same either way; only the work differs.
+// ---------------------------------------------------------------------------
+constexpr int kSampleBlocks = 32, kSampleBlock = 256;  // 8192 sampled keys, 8 per thread
+constexpr int kSampleRowMin = 65536;                   // rows at least this long are sampled
+static_assert(kSampleBlocks * kSampleBlock == 8 * kThreads, "8 sampled keys per thread");
+
+// The bound tau, or 0 when the sample cannot give a useful one (too few
+// selectable sampled keys, or a k too large for the gathered set).  Every
+// thread must call it and gets the same value.  Rows of n >= kSampleRowMin.
+template <bool FORCED>
+__device__ uint32_t sample_bound(const float *row, int n, int k, int f_lo, int f_hi, CutLds<kThreads> *L) {
+    const int tid = threadIdx.x;
+    constexpr int TPB = kSampleBlock / 8;  // threads per sampled block
+    const int j = tid / TPB;
+    const int i0 = (int)((int64_t)j * (n - kSampleBlock) / (kSampleBlocks - 1)) + (tid % TPB) * 8;
+    unsigned long long e[8];
+    int cnt = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+        const int i = i0 + q;
+        const uint32_t u = select_key<FORCED>(row[i], i, f_lo, f_hi);
+        e[q] = u ? stream_entry(u, i) : 0ull;
+        cnt += u != 0;
+    }
+    int total;
+    (void)block_excl_scan<kThreads>(cnt, L, &total);
+    // sampled ranks [lo, hi] stand for about 1.4 k .. 1.5 k row keys
+    constexpr int64_t ns = kSampleBlocks * kSampleBlock;
+    int lo = (int)((14LL * k * ns + 10LL * n - 1) / (10LL * n));
+    int hi = (int)((15LL * k * ns) / (10LL * n));
+    lo = max(lo, 48);
+    hi = max(hi, lo + 8);
+    if ((int64_t)hi * n > (int64_t)(kLongS * 4 / 5) * ns || total <= lo) return 0u;
+    const unsigned long long b = cut_bound<kThreads, 8>([&](int q) { return e[q]; }, lo, hi, L);
+    return (uint32_t)(b >> 32);
+}
+
+// One pass over the row: *nsel gets its selectable keys, and every key >=
+// tau (> 0) is appended to S (up to kLongS of them; sc[3] counts them all
+// and must be 0 on entry).  A wave claims its slots with one LDS atomic per
+// batch of loads; the loop bounds are the same for every thread, so every
+// wave runs its appends whole.  The pass appends indices only; when they
+// all fit, a short loop then re-reads their scores (just read, so cached)
+// and completes the entries, so no score has to be picked out of a
+// thread's loads by a runtime index.  Every thread must call it; ends with
+// a barrier, after which sc[3] and S are final.
+//
+// Without forced keys the tests run on the floats: the key map is monotonic
+// (NaN and -inf map to 0, -0 ties with +0), and tau is the key of a finite
+// or infinite score (at least that of -FLT_MAX), so key(x) >= tau exactly
+// when x >= value(tau), and a key is selectable exactly when x > -inf.
+template <bool FORCED>
+__device__ void gather_above(const float *row, int n, uint32_t tau, int f_lo, int f_hi, unsigned long long *S,
+                             int *sc, int *nsel) {
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const float ftau = __builtin_bit_cast(float, (tau & 0x80000000u) ? (tau & 0x7fffffffu) : ~tau);
+    int cnt = 0;
+    // appends the indices of the set bits of `hits` (bit b: index
+    // idx_of(b)); a lane loops over its own set bits only
+    auto append = [&](uint32_t hits, auto &&idx_of) {
+        const int h = __popc(hits);
+        const int incl = wave_incl_scan(h);
+        const int wtot = __builtin_amdgcn_readlane(incl, 63);
+        if (wtot == 0) return;
+        int base = 0;
+        if (lane == 63) base = (int)atomicAdd((uint32_t *)&sc[3], (uint32_t)wtot);
+        base = __builtin_amdgcn_readlane(base, 63);
+        int pos = base + incl - h;
+        while (hits) {
+            const int bit = __builtin_ctz(hits);
+            hits &= hits - 1u;
+            if (pos < kLongS) S[pos] = (uint32_t)(~(uint32_t)idx_of(bit));
+            ++pos;
+        }
+    };
+    auto test = [&](int i, float x) -> uint32_t {
+        if constexpr (FORCED) {
+            const uint32_t u = select_key<FORCED>(x, i, f_lo, f_hi);
+            cnt += u != 0;
+            return u >= tau ? 1u : 0u;
+        } else {
+            (void)i;
+            cnt += x > -INFINITY;
+            return x >= ftau ? 1u : 0u;
+        }
+    };
+    int done = 0;  // keys handled by the 16-byte loops
+    if (((uintptr_t)row & 15) == 0) {
+        const int n4 = n >> 2;
+        const float4 *r4 = reinterpret_cast<const float4 *>(row);
+        int i0 = 0;
+        for (; i0 + 4 * kThreads <= n4; i0 += 4 * kThreads) {  // four 16-byte loads per thread in flight
+            const int i = i0 + tid;
+            float4 v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = r4[i + u * kThreads];
+            uint32_t hits = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int b = (i + u * kThreads) * 4;
+                hits |= test(b, v[u].x) << (4 * u);
+                hits |= test(b + 1, v[u].y) << (4 * u + 1);
+                hits |= test(b + 2, v[u].z) << (4 * u + 2);
+                hits |= test(b + 3, v[u].w) << (4 * u + 3);
+            }
+            append(hits, [&](int bit) { return (i + (bit >> 2) * kThreads) * 4 + (bit & 3); });
+        }
+        for (; i0 < n4; i0 += kThreads) {  // the remaining 16-byte chunks, one per thread
+            const int ii = i0 + tid;
+            float4 w = make_float4(-INFINITY, -INFINITY, -INFINITY, -INFINITY);
+            uint32_t hits = 0;
+            if (ii < n4) {
+                w = r4[ii];
+                hits |= test(4 * ii, w.x);
+                hits |= test(4 * ii + 1, w.y) << 1;
+                hits |= test(4 * ii + 2, w.z) << 2;
+                hits |= test(4 * ii + 3, w.w) << 3;
+            }
+            append(hits, [&](int bit) { return 4 * ii + bit; });
+        }
+        done = 4 * n4;
+    }
+    for (int j0 = done; j0 < n; j0 += kThreads) {  // the tail, or a row not 16-byte aligned
+        const int jj = j0 + tid;
+        float x = -INFINITY;
+        uint32_t hits = 0;
+        if (jj < n) {
+            x = row[jj];
+            hits = test(jj, x);
+        }
+        append(hits, [&](int) { return jj; });
+    }
+    cnt = wave_sum(cnt);
+    if (lane == 0) sc[8 + wid] = cnt;
+    __syncthreads();
+    *nsel = waves_sum<kWaves>(sc + 8);
+    const int got = sc[3];
+    if (got <= kLongS) {
+        for (int q = tid; q < got; q += kThreads) {
+            const int i = (int)~(uint32_t)S[q];
+            S[q] = ((unsigned long long)select_key<FORCED>(row[i], i, f_lo, f_hi) << 32) | (uint32_t)(~(uint32_t)i);
+        }
+        __syncthreads();
+    }
+}
+
 template <bool FORCED>
 __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int k_pad) {
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -461,89 +621,109 @@ __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int 
         return ((unsigned long long)u << 32) | (uint32_t)(~(uint32_t)i);
     };
 
-    // ---- 1. count, min, max, and a histogram of the keys' top 12 bits ------
-    for (int i = tid; i < 4096; i += kThreads) hist[i] = 0u;
-    __syncthreads();
-    int cnt = 0;
-    uint32_t mn = 0xffffffffu, mx = 0u;
-    stream_row(row, n, [&](int i, float x) {
-        const uint32_t u = select_key<FORCED>(x, i, f_lo, f_hi);
-        if (u) {
-            ++cnt;
-            mn = min(mn, u);
-            mx = max(mx, u);
-            atomicAdd(&hist[u >> 20], 1u);
+    // ---- 0. the sampled one-pass gather (rows long enough to sample) -------
+    int total_sel = 0, m = 0;
+    bool gathered = false;
+    if (n >= kSampleRowMin) {
+        if (tid == 0) sc[3] = 0;  // published by the barriers in sample_bound
+        const uint32_t tau = sample_bound<FORCED>(row, n, k, f_lo, f_hi, reinterpret_cast<CutLds<kThreads> *>(smem));
+        if (tau != 0u) {
+            int nsel_f;
+            gather_above<FORCED>(row, n, tau, f_lo, f_hi, S, sc, &nsel_f);
+            const int got = sc[3];
+            if (nsel_f > k && got >= k && got <= kLongS) {
+                gathered = true;
+                total_sel = k;
+                m = got;
+            }
         }
-    });
-    cnt = wave_sum(cnt);
-    mn = wave_min_u32(mn);
-    mx = wave_max_u32(mx);
-    if (lane == 0) {
-        sc[8 + wid] = cnt;
-        sc[8 + kWaves + wid] = (int)mn;
-        sc[8 + 2 * kWaves + wid] = (int)mx;
+        __syncthreads();  // every thread has read sc before the passes below may reuse it
     }
-    if (tid == 0) sc[3] = 0;
-    __syncthreads();
-    const int nsel = waves_sum<kWaves>(sc + 8);
-    mn = waves_min_u32<kWaves>(sc + 8 + kWaves);
-    mx = waves_max_u32<kWaves>(sc + 8 + 2 * kWaves);
-    const bool all = nsel <= k;
-    const int total_sel = all ? nsel : k;
-    for (int j = total_sel + tid; j < k; j += kThreads) {
-        idx_out[j] = -1;
-        if (val_out) val_out[j] = -INFINITY;
-    }
-    if (nsel == 0) return;
+    if (!gathered) {
+        // ---- 1. count, min, max, and a histogram of the keys' top 12 bits ------
+        for (int i = tid; i < 4096; i += kThreads) hist[i] = 0u;
+        __syncthreads();
+        int cnt = 0;
+        uint32_t mn = 0xffffffffu, mx = 0u;
+        stream_row(row, n, [&](int i, float x) {
+            const uint32_t u = select_key<FORCED>(x, i, f_lo, f_hi);
+            if (u) {
+                ++cnt;
+                mn = min(mn, u);
+                mx = max(mx, u);
+                atomicAdd(&hist[u >> 20], 1u);
+            }
+        });
+        cnt = wave_sum(cnt);
+        mn = wave_min_u32(mn);
+        mx = wave_max_u32(mx);
+        if (lane == 0) {
+            sc[8 + wid] = cnt;
+            sc[8 + kWaves + wid] = (int)mn;
+            sc[8 + 2 * kWaves + wid] = (int)mx;
+        }
+        if (tid == 0) sc[3] = 0;
+        __syncthreads();
+        const int nsel = waves_sum<kWaves>(sc + 8);
+        mn = waves_min_u32<kWaves>(sc + 8 + kWaves);
+        mx = waves_max_u32<kWaves>(sc + 8 + 2 * kWaves);
+        const bool all = nsel <= k;
+        total_sel = all ? nsel : k;
+        for (int j = total_sel + tid; j < k; j += kThreads) {
+            idx_out[j] = -1;
+            if (val_out) val_out[j] = -INFINITY;
+        }
+        if (nsel == 0) return;
 
-    // ---- 2. boundary bin: of the top-12-bit histogram when its bin is small
-    // enough to gather, else of a second histogram of the 12 bits below the
-    // common prefix of the row's largest and smallest keys (the same bins
-    // when the row has keys of both signs) ---------------------------------
-    int B = -1, shift = 0, nb = 1;
-    if (!all) {
-        if (mn == mx) {  // every selectable key equal: index order decides
-            __syncthreads();
-            topk_row_general<FORCED>(a, k_pad, smem);
-            return;
-        }
-        scan_bins_desc(hist, nullptr, 4096, k, sc);
-        const int cnt_top = sc[2];
-        __syncthreads();  // every thread has read sc[2] before it may change
-        if (cnt_top <= kLongCand) {
-            B = sc[0];
-            shift = 20;
-            nb = 4096;
-        } else {
-            const int pos = 32 - __clz(mn ^ mx);
-            const int width = pos < 12 ? pos : 12;
-            shift = pos - width;
-            nb = 1 << width;
-            for (int i = tid; i < 4096; i += kThreads) hist[i] = 0u;
-            __syncthreads();
-            stream_row(row, n, [&](int i, float x) {
-                const uint32_t u = select_key<FORCED>(x, i, f_lo, f_hi);
-                if (u) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
-            });
-            __syncthreads();
-            scan_bins_desc(hist, nullptr, nb, k, sc);
-            B = sc[0];
-            const int cnt_b = sc[2];
-            if (cnt_b > kLongCand) {
+        // ---- 2. boundary bin: of the top-12-bit histogram when its bin is small
+        // enough to gather, else of a second histogram of the 12 bits below the
+        // common prefix of the row's largest and smallest keys (the same bins
+        // when the row has keys of both signs) ---------------------------------
+        int B = -1, shift = 0, nb = 1;
+        if (!all) {
+            if (mn == mx) {  // every selectable key equal: index order decides
                 __syncthreads();
                 topk_row_general<FORCED>(a, k_pad, smem);
                 return;
             }
+            scan_bins_desc(hist, nullptr, 4096, k, sc);
+            const int cnt_top = sc[2];
+            __syncthreads();  // every thread has read sc[2] before it may change
+            if (cnt_top <= kLongCand) {
+                B = sc[0];
+                shift = 20;
+                nb = 4096;
+            } else {
+                const int pos = 32 - __clz(mn ^ mx);
+                const int width = pos < 12 ? pos : 12;
+                shift = pos - width;
+                nb = 1 << width;
+                for (int i = tid; i < 4096; i += kThreads) hist[i] = 0u;
+                __syncthreads();
+                stream_row(row, n, [&](int i, float x) {
+                    const uint32_t u = select_key<FORCED>(x, i, f_lo, f_hi);
+                    if (u) atomicAdd(&hist[(u >> shift) & (nb - 1)], 1u);
+                });
+                __syncthreads();
+                scan_bins_desc(hist, nullptr, nb, k, sc);
+                B = sc[0];
+                const int cnt_b = sc[2];
+                if (cnt_b > kLongCand) {
+                    __syncthreads();
+                    topk_row_general<FORCED>(a, k_pad, smem);
+                    return;
+                }
+            }
         }
-    }
 
-    // ---- 3. gather every key of a bin >= B ----------------------------------
-    stream_row(row, n, [&](int i, float x) {
-        const uint32_t u = select_key<FORCED>(x, i, f_lo, f_hi);
-        if (u && (int)((u >> shift) & (nb - 1)) >= B) S[atomicAdd((uint32_t *)&sc[3], 1u)] = pack(i, u);
-    });
-    __syncthreads();
-    const int m = sc[3];
+        // ---- 3. gather every key of a bin >= B ----------------------------------
+        stream_row(row, n, [&](int i, float x) {
+            const uint32_t u = select_key<FORCED>(x, i, f_lo, f_hi);
+            if (u && (int)((u >> shift) & (nb - 1)) >= B) S[atomicAdd((uint32_t *)&sc[3], 1u)] = pack(i, u);
+        });
+        __syncthreads();
+        m = sc[3];
+    }  // steps 1-3
 
     // ---- 4. select and order the gathered set ------------------------------
     uint32_t smn = 0xffffffffu, smx = 0u;
@@ -565,12 +745,17 @@ __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int 
     smx = waves_max_u32<kWaves>(sc + 16 + kWaves);
     bool sorted_out = false;
     if (smn != smx) {
-        const int pos2 = 32 - __clz(smn ^ smx);
-        const int width2 = pos2 < 11 ? pos2 : 11;
-        const int shift2 = pos2 - width2;
-        const int nb2 = 1 << width2;
-        for (int q = tid; q < m; q += kThreads)
-            atomicAdd(&hist[(uint32_t)(S[q] >> (32 + shift2)) & (nb2 - 1)], 1u);
+        // bins of the key's distance from the set's smallest key: order
+        // preserving, and spread over up to 2048 bins wherever the set's
+        // scores lie (bins of a common bit prefix collapse when the set
+        // straddles a power of two whose exponent bits all differ, 2.0
+        // say, and its ordering then falls back to the bitonic sort)
+        const uint32_t span = smx - smn;
+        const int bits = 32 - __clz(span);
+        const int shift2 = bits > 11 ? bits - 11 : 0;
+        const int nb2 = 1 << (32 - __clz(span >> shift2));  // a power of two above the largest bin, <= 2048
+        auto bin2 = [&](unsigned long long e) { return (int)(((uint32_t)(e >> 32) - smn) >> shift2); };
+        for (int q = tid; q < m; q += kThreads) atomicAdd(&hist[bin2(S[q])], 1u);
         __syncthreads();
         scan_bins_desc(hist, hcur, nb2, total_sel, sc);
         const int bmax = (int)waves_max_u32<kWaves>(sc + 8);
@@ -579,14 +764,14 @@ __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int 
             const int start2 = total_sel - need2;
             for (int q = tid; q < m; q += kThreads) {
                 const unsigned long long e = S[q];
-                const int d = (int)((uint32_t)(e >> (32 + shift2)) & (nb2 - 1));
+                const int d = bin2(e);
                 if (d > B2) O[atomicAdd(&hcur[d], 1u)] = e;
                 else if (d == B2) cand2[atomicAdd((uint32_t *)&sc[4], 1u)] = e;
             }
             __syncthreads();
             for (int j = tid; j < start2; j += kThreads) {
                 const unsigned long long e = O[j];
-                const uint32_t d = (uint32_t)(e >> (32 + shift2)) & (nb2 - 1);
+                const int d = bin2(e);
                 const int c = (int)hist[d];
                 const int s0 = (int)hcur[d] - c;
                 int rank = 0;

@@ -561,7 +561,7 @@ def test_topk_row_len_and_short_rows():
 
 
 @pytest.mark.parametrize("n_cols", [1, 255, 1024, 1025, 2048, 4096, 5000, 8192, 12000, 16384, 16385,
-                                    40000, 131072])
+                                    40000, 65535, 65536, 100003, 131072])
 def test_topk_row_lengths(n_cols):
     rng = np.random.default_rng(n_cols)
     rows = 8
@@ -578,6 +578,50 @@ def test_topk_row_lengths(n_cols):
     for k in (1, 31, 64, 512, 2048):
         gi, gv = gpu_topk(dev(s), k)
         check_topk_exact(gi, gv, s, k, where=f"n_cols={n_cols} k={k}")
+
+
+def test_topk_long_rows_with_periodic_structure():
+    """Long rows whose large scores sit in evenly spaced blocks of 256 keys,
+    or everywhere but in them (a structure a sampled estimate of the k-th
+    score would misjudge both ways), and rows with a few large values: equal
+    bit for bit to the oracle's selection of the same f32 scores."""
+    rng = np.random.default_rng(17)
+    n = 131072
+    s = rng.standard_normal((6, n)).astype(np.float32)
+    blocks = np.zeros(n, dtype=bool)
+    for j in range(32):
+        b0 = j * (n - 256) // 31
+        blocks[b0:b0 + 256] = True
+    s[0, blocks] += 100.0          # large values only in the blocks
+    s[1, ~blocks] += 100.0         # large values everywhere else
+    s[2, blocks] = -np.inf         # the blocks hold nothing selectable
+    s[3, rng.permutation(n)[:1500]] += 50.0   # fewer large values than k
+    s[4, blocks] = 7.0             # the blocks tie on one value
+    s[5, ::3] = np.round(s[5, ::3] * 4) / 4   # many ties near every score
+    row_len = np.array([n, n, n, n, n - 1000, 70001], dtype=np.int32)
+    for k in (64, 2048):
+        for rl in (None, row_len):
+            gi, gv = gpu_topk(dev(s), k, None if rl is None else dev(rl))
+            check_topk_exact(gi, gv, s, k, rl, where=f"periodic k={k} row_len={rl is not None}")
+
+
+def test_topk_long_rows_straddling_a_power_of_two():
+    """Long rows whose best few thousand scores lie just either side of 2.0
+    (whose float exponent bits all differ from those just below it), or of
+    0, or on a few values only: the gathered set is ordered by bins of key
+    distance, equal bit for bit to the oracle's selection."""
+    rng = np.random.default_rng(23)
+    n = 131072
+    s = rng.uniform(0.0, 1.9, size=(4, n)).astype(np.float32)
+    top = rng.permutation(n)[:4000]
+    s[0, top] = rng.uniform(1.95, 2.05, size=4000).astype(np.float32)
+    s[1, top] = rng.uniform(-0.01, 0.01, size=4000).astype(np.float32) + 3.0 * (rng.random(4000) < 0.3)
+    s[2] = -s[2]
+    s[2, top] = rng.uniform(-0.05, 0.05, size=4000).astype(np.float32)   # around zero, both signs
+    s[3, top] = np.round(rng.uniform(1.95, 2.05, size=4000) * 64).astype(np.float32) / 64   # few values, ties
+    for k in (100, 2048):
+        gi, gv = gpu_topk(dev(s), k)
+        check_topk_exact(gi, gv, s, k, where=f"straddle k={k}")
 
 
 @pytest.mark.parametrize("n_rows", [4, 520])
@@ -616,7 +660,7 @@ def test_topk_many_rows_heavy_ties():
 
 # ------------------------------------------------------------ block ranking
 
-@pytest.mark.parametrize("n_cols", [300, 5000, 16384, 40000])
+@pytest.mark.parametrize("n_cols", [300, 5000, 16384, 40000, 131072])
 def test_topk_blocks_rows(n_cols):
     """Block ranking on every top-k kernel (row kernels of 512 and 1024
     threads, the streaming long-row kernel): ties, -inf, NaN, row lengths
