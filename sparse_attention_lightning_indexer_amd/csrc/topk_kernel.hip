@@ -7,9 +7,9 @@
 // reported values are the keys mapped back (a zero is re-read from the row,
 // so that -0 is reported as stored).  Three kernels, by row length:
 //  * rows of up to 16384 keys (topk_rows_kernel): one workgroup per row, the
-//    keys register-resident.  Fast path: one histogram of the 12 bits just
-//    below the common prefix of the row's largest and smallest selectable
-//    keys selects and orders at once (a descending scan gives every bin its
+//    keys register-resident.  Fast path: one histogram of up to 4096 bins of
+//    the keys' distance from the row's smallest selectable key selects and
+//    orders at once (a descending scan gives every bin its
 //    output offset; a key's position is its bin's offset plus its rank inside
 //    the bin).  Crowded bins take an adaptive 12-bit radix select, an
 //    index-ordered compaction and a bucketed or bitonic ordering.
@@ -968,8 +968,11 @@ __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_ker
     };
 
     // ---- fast path: one 12-bit histogram serves as both the select and the
-    // ordering buckets.  Bins are the 12 bits just below the common prefix of
-    // the row's largest and smallest selectable keys.  A descending scan gives
+    // ordering buckets.  Bins are the keys' distance from the row's smallest
+    // selectable key, scaled to at most 4096 (2048) bins: order preserving,
+    // and spread over the row's range wherever it lies (bins of a common bit
+    // prefix collapse for rows that straddle a power of two whose exponent
+    // bits all differ, 2.0 say).  A descending scan gives
     // every bin its output offset and finds the bin B holding the last
     // selected position; keys in higher bins are placed by their rank inside
     // their bin, the keys of B are ranked among themselves and the best of
@@ -977,17 +980,17 @@ __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_ker
     // Rows with a bin of more than kMaxBucket selected keys, or more than
     // kMaxCand keys in B, take the general path below instead.
     {
-        const uint32_t diff = mn ^ mx;
-        const int pos = diff ? 32 - __clz(diff) : 0;
-        if (nsel > 0 && pos > 0) {
-            const int width = pos < BITS ? pos : BITS;
-            const int shift = pos - width;
-            const int nb = 1 << width;
+        const uint32_t span = mx - mn;
+        if (nsel > 0 && mx != mn) {
+            const int bits = 32 - __clz(span);
+            const int shift = bits > BITS ? bits - BITS : 0;
+            const int nb = 1 << (32 - __clz(span >> shift));  // a power of two above the largest bin
+            auto bin = [&](uint32_t u) { return (int)((u - mn) >> shift); };
             const bool all0 = nsel <= k;
             const int sel_total = all0 ? nsel : k;
 #pragma unroll
             for (int j = 0; j < E; ++j)
-                if (key[j]) atomicAdd(&hist0[(key[j] >> shift) & (nb - 1)], 1u);
+                if (key[j]) atomicAdd(&hist0[bin(key[j])], 1u);
             __syncthreads();
             // descending exclusive scan of the bin counts
             constexpr int MAXPER = NBINS / THREADS;
@@ -1021,7 +1024,7 @@ __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_ker
                 for (int j = 0; j < E; ++j) {
                     const uint32_t u = key[j];
                     if (!u) continue;
-                    const int d = (int)((u >> shift) & (nb - 1));
+                    const int d = bin(u);
                     const unsigned long long e =
                         ((unsigned long long)u << 32) | (uint32_t)(~(uint32_t)(tid + THREADS * j));
                     if (d > B) sel[atomicAdd(&hist1[d], 1u)] = e;
@@ -1035,7 +1038,7 @@ __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_ker
                 // whole bins: position = bin start + rank inside the bin
                 for (int j = tid; j < start_b; j += THREADS) {
                     const unsigned long long e = sel[j];
-                    const uint32_t d = (uint32_t)(e >> (32 + shift)) & (nb - 1);
+                    const int d = bin((uint32_t)(e >> 32));
                     const int cnt = (int)hist0[d];
                     const int s0 = (int)hist1[d] - cnt;
                     int rank = 0;

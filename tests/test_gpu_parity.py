@@ -624,6 +624,24 @@ def test_topk_long_rows_straddling_a_power_of_two():
         check_topk_exact(gi, gv, s, k, where=f"straddle k={k}")
 
 
+@pytest.mark.parametrize("n_rows", [8, 600])
+def test_topk_rows_straddling_a_power_of_two(n_rows):
+    """Register-resident rows (one per 1024 or per 512 threads) whose scores
+    lie around 2.0, around 0 with both signs, or around 2.0 on a few values:
+    the histogram bins are key distances, and the result is bit for bit the
+    oracle's selection."""
+    rng = np.random.default_rng(29 + n_rows)
+    n = 5000
+    s = (2.0 + 0.3 * rng.standard_normal((n_rows, n))).astype(np.float32)
+    s[1::3] = (0.05 * rng.standard_normal((len(s[1::3]), n))).astype(np.float32)
+    s[2::3] = np.round(s[2::3] * 32) / 32
+    row_len = rng.integers(1, n + 1, size=n_rows).astype(np.int32)
+    for k in (64, 512, 2048):
+        for rl in (None, row_len):
+            gi, gv = gpu_topk(dev(s), k, None if rl is None else dev(rl))
+            check_topk_exact(gi, gv, s, k, rl, where=f"straddle rows={n_rows} k={k}")
+
+
 @pytest.mark.parametrize("n_rows", [4, 520])
 def test_topk_selection_ends_at_a_bin_edge(n_rows):
     """Rows whose best keys fill the top histogram bins exactly (k = 8, 15),
