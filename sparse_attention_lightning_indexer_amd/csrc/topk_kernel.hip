@@ -489,9 +489,9 @@ __device__ uint32_t sample_bound(const float *row, int n, int k, int f_lo, int f
 // tau (> 0) is appended to S (up to kLongS of them; sc[3] counts them all
 // and must be 0 on entry).  A wave claims its slots with one LDS atomic per
 // batch of loads; the loop bounds are the same for every thread, so every
-// wave runs its appends whole.  The pass appends indices only; when they
-// all fit, a short loop then re-reads their scores (just read, so cached)
-// and completes the entries, so no score has to be picked out of a
+// wave runs its appends whole.  An appended key's score is read again
+// from the row right away (its line was loaded moments before, so the read
+// is served by the cache), so that no score has to be picked out of a
 // thread's loads by a runtime index.  Every thread must call it; ends with
 // a barrier, after which sc[3] and S are final.
 //
@@ -505,8 +505,8 @@ __device__ void gather_above(const float *row, int n, uint32_t tau, int f_lo, in
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
     const float ftau = __builtin_bit_cast(float, (tau & 0x80000000u) ? (tau & 0x7fffffffu) : ~tau);
     int cnt = 0;
-    // appends the indices of the set bits of `hits` (bit b: index
-    // idx_of(b)); a lane loops over its own set bits only
+    // appends the keys of the set bits of `hits` (bit b: index idx_of(b));
+    // a lane loops over its own set bits only
     auto append = [&](uint32_t hits, auto &&idx_of) {
         const int h = __popc(hits);
         const int incl = wave_incl_scan(h);
@@ -519,7 +519,11 @@ __device__ void gather_above(const float *row, int n, uint32_t tau, int f_lo, in
         while (hits) {
             const int bit = __builtin_ctz(hits);
             hits &= hits - 1u;
-            if (pos < kLongS) S[pos] = (uint32_t)(~(uint32_t)idx_of(bit));
+            if (pos < kLongS) {
+                const int i = idx_of(bit);
+                S[pos] = ((unsigned long long)select_key<FORCED>(row[i], i, f_lo, f_hi) << 32) |
+                         (uint32_t)(~(uint32_t)i);
+            }
             ++pos;
         }
     };
@@ -584,14 +588,6 @@ __device__ void gather_above(const float *row, int n, uint32_t tau, int f_lo, in
     if (lane == 0) sc[8 + wid] = cnt;
     __syncthreads();
     *nsel = waves_sum<kWaves>(sc + 8);
-    const int got = sc[3];
-    if (got <= kLongS) {
-        for (int q = tid; q < got; q += kThreads) {
-            const int i = (int)~(uint32_t)S[q];
-            S[q] = ((unsigned long long)select_key<FORCED>(row[i], i, f_lo, f_hi) << 32) | (uint32_t)(~(uint32_t)i);
-        }
-        __syncthreads();
-    }
 }
 
 template <bool FORCED>
