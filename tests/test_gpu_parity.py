@@ -928,3 +928,39 @@ def test_floor_probes():
     buf = torch.zeros(1 << 20, dtype=torch.float32, device=DEV)
     pp.read(buf, pp.sink_for(DEV))
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_topk_randomized_sweep(seed):
+    """Seeded random shapes through every top-k kernel (register rows of 512
+    and 1024 threads, the long-row kernel with and without its sampled pass,
+    block ranking): row lengths around the kernels' limits, k from 1 to
+    2048, and score mixes of ties, -inf, NaN, both signs and narrow ranges;
+    bit for bit the oracle's selection of the same f32 scores."""
+    rng = np.random.default_rng(1000 + seed)
+    n_cols = int(rng.choice([3000, 9000, 16384, 16385, 40000, 65535, 65536, 70001, 131072]))
+    n_rows = int(rng.choice([3, 8, 600])) if n_cols <= 16384 else int(rng.choice([3, 8]))
+    k = int(rng.choice([1, 7, 64, 333, 512, 1024, 2048]))
+    kind = seed % 4
+    if kind == 0:
+        s = rng.standard_normal((n_rows, n_cols)) * rng.uniform(0.1, 100.0)
+    elif kind == 1:
+        s = rng.integers(-50, 50, size=(n_rows, n_cols)).astype(np.float64)   # heavy ties
+    elif kind == 2:
+        s = 2.0 + rng.standard_normal((n_rows, n_cols)) * 0.02                  # narrow, around 2.0
+    else:
+        s = np.exp(rng.standard_normal((n_rows, n_cols)) * 3.0) * np.sign(rng.standard_normal((n_rows, n_cols)))
+    s = s.astype(np.float32)
+    s[rng.random(s.shape) < rng.uniform(0.0, 0.5)] = -np.inf
+    s[rng.random(s.shape) < 0.001] = np.nan
+    row_len = rng.integers(0, n_cols + 1, size=n_rows).astype(np.int32)
+    row_len[0] = n_cols
+    gi, gv = gpu_topk(dev(s), k, dev(row_len))
+    check_topk_exact(gi, gv, s, k, row_len, where=f"sweep seed={seed} n={n_cols} rows={n_rows} k={k} kind={kind}")
+    if seed % 3 == 0:
+        init, local = int(rng.integers(0, 300)), int(rng.integers(0, 300))
+        bi, bv = li.topk_blocks(dev(s), k, init, local, dev(row_len))
+        torch.cuda.synchronize()
+        oi, ov = oracle.topk_blocks(s, k, init, local, row_len)
+        assert np.array_equal(bi.cpu().numpy(), oi), f"sweep blocks seed={seed}"
+        assert np.array_equal(bv.cpu().numpy().view(np.uint32), ov.view(np.uint32))
