@@ -964,3 +964,33 @@ def test_topk_randomized_sweep(seed):
         oi, ov = oracle.topk_blocks(s, k, init, local, row_len)
         assert np.array_equal(bi.cpu().numpy(), oi), f"sweep blocks seed={seed}"
         assert np.array_equal(bv.cpu().numpy().view(np.uint32), ov.view(np.uint32))
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_score_randomized_sweep(seed):
+    """Seeded random shapes through the score kernels and the fused paths:
+    prefill and paged decode, head counts from 1 to 100 (compiled, padded
+    and in passes), head dimensions from 8 to 256, every mask and weight
+    kind, visible prefixes, query lengths and block sizes; scores against
+    the fp64 oracle, top-k bit for bit, fused equal to score then top-k."""
+    rng = np.random.default_rng(2000 + seed)
+    H = int(rng.choice([1, 3, 4, 8, 12, 16, 32, 48, 64, 100]))
+    d = int(rng.choice([8, 24, 64, 72, 128, 200, 256]))
+    w_kind = str(rng.choice(["uniform", "equal", "signed", "pow2"]))
+    if seed % 2 == 0:
+        T, P = int(rng.integers(1, 40)), int(rng.integers(1, 700))
+        k_top = int(rng.integers(1, min(P, 2048) + 1))
+        mask_kind = str(rng.choice(["none", "zero", "random", "causal", "bias", "all_inf"]))
+        vis_kind = str(rng.choice(["none", "random"]))
+        inp = W.random_prefill(3000 + seed, T, P, H, d, k_top, mask_kind=mask_kind, w_kind=w_kind, vis_kind=vis_kind)
+        where = f"sweep prefill seed={seed} T={T} P={P} H={H} d={d} k={k_top} {mask_kind}/{w_kind}/{vis_kind}"
+    else:
+        R, Q = int(rng.integers(1, 9)), int(rng.choice([1, 2, 4]))
+        bs = int(rng.choice([1, 4, 16, 64]))
+        lo = int(rng.integers(0, 300))
+        hi = lo + int(rng.integers(0, 500))
+        k_top = int(rng.integers(1, 257))
+        mask_kind = str(rng.choice(["none", "random", "bias"]))
+        inp = W.random_decode(3000 + seed, R, Q, H, d, bs, lo, hi, k_top, w_kind=w_kind, mask_kind=mask_kind)
+        where = f"sweep decode seed={seed} R={R} Q={Q} H={H} d={d} bs={bs} len={lo}..{hi} k={k_top} {mask_kind}/{w_kind}"
+    _full_check(inp, where)
