@@ -966,13 +966,15 @@ def test_topk_randomized_sweep(seed):
         assert np.array_equal(bv.cpu().numpy().view(np.uint32), ov.view(np.uint32))
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(64))
 def test_score_randomized_sweep(seed):
     """Seeded random shapes through the score kernels and the fused paths:
     prefill and paged decode, head counts from 1 to 100 (compiled, padded
     and in passes), head dimensions from 8 to 256, every mask and weight
     kind, visible prefixes, query lengths and block sizes; scores against
-    the fp64 oracle, top-k bit for bit, fused equal to score then top-k."""
+    the fp64 oracle, top-k bit for bit, fused equal to score then top-k,
+    and (prefill, one pass over the heads) the streaming path equal to the
+    fused one."""
     rng = np.random.default_rng(2000 + seed)
     H = int(rng.choice([1, 3, 4, 8, 12, 16, 32, 48, 64, 100]))
     d = int(rng.choice([8, 24, 64, 72, 128, 200, 256]))
@@ -984,6 +986,13 @@ def test_score_randomized_sweep(seed):
         vis_kind = str(rng.choice(["none", "random"]))
         inp = W.random_prefill(3000 + seed, T, P, H, d, k_top, mask_kind=mask_kind, w_kind=w_kind, vis_kind=vis_kind)
         where = f"sweep prefill seed={seed} T={T} P={P} H={H} d={d} k={k_top} {mask_kind}/{w_kind}/{vis_kind}"
+        if H <= (32 if d > 128 else 64):
+            fi, fv = gpu_fused(inp)
+            si, sv = li.score_topk_stream_prefill(dev(inp.q), dev(inp.k), dev(inp.w), k_top, dev(inp.mask),
+                                                  dev(inp.vis_len))
+            torch.cuda.synchronize()
+            assert np.array_equal(si.cpu().numpy(), fi), f"{where}: streaming indices differ"
+            assert np.array_equal(sv.cpu().numpy().view(np.uint32), fv.view(np.uint32)), f"{where}: streaming values differ"
     else:
         R, Q = int(rng.integers(1, 9)), int(rng.choice([1, 2, 4]))
         bs = int(rng.choice([1, 4, 16, 64]))
