@@ -38,12 +38,15 @@ constexpr int kDigits = 3;  // bits 31:21, 20:10, 9:0
 __device__ __forceinline__ int digit_shift(int p) { return p == 0 ? 21 : (p == 1 ? 10 : 0); }
 __device__ __forceinline__ int digit_width(int p) { return p == 2 ? 10 : 11; }
 
+// Order-preserving u32 key of a score: a negative score maps to the two's
+// complement of its bit pattern (so -0 lands on the key of +0, 0x80000000),
+// the rest keep their bits with the top one set; NaN and -inf map to 0 and
+// are never selected.  Selectable keys lie in [0x00800001, 0xff800000]
+// (-FLT_MAX .. +inf).
 __device__ __forceinline__ uint32_t order_key(float x) {
-    uint32_t u = __builtin_bit_cast(uint32_t, x);
-    if (x != x) return 0u;             // NaN: never selected
-    if (u == 0xff800000u) return 0u;   // -inf: never selected
-    if (u == 0x80000000u) u = 0u;      // -0 ties with +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+    const uint32_t b = __builtin_bit_cast(uint32_t, x);
+    const uint32_t u = (int)b < 0 ? 0u - b : (b | 0x80000000u);
+    return x > -INFINITY ? u : 0u;
 }
 
 // Block ranking (the vLLM decode kernel's init_blocks / local_blocks): the
@@ -85,7 +88,7 @@ __device__ __forceinline__ uint32_t select_key(float x, int s, int f_lo, int f_h
 // so is a forced key's score.
 __device__ __forceinline__ float key_value(uint32_t u, const float *row, int s) {
     if (u == 0x80000000u || u == kForcedKey) return row[s];
-    return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7fffffffu) : ~u);
+    return __builtin_bit_cast(float, (u & 0x80000000u) ? (u & 0x7fffffffu) : 0u - u);
 }
 
 __device__ __forceinline__ unsigned long long lanes_below(int lane) {
@@ -503,7 +506,7 @@ template <bool FORCED>
 __device__ void gather_above(const float *row, int n, uint32_t tau, int f_lo, int f_hi, unsigned long long *S,
                              int *sc, int *nsel) {
     const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const float ftau = __builtin_bit_cast(float, (tau & 0x80000000u) ? (tau & 0x7fffffffu) : ~tau);
+    const float ftau = __builtin_bit_cast(float, (tau & 0x80000000u) ? (tau & 0x7fffffffu) : 0u - tau);
     int cnt = 0;
     // appends the keys of the set bits of `hits` (bit b: index idx_of(b));
     // a lane loops over its own set bits only
@@ -923,37 +926,38 @@ __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_ker
     const int f_lo = forced_lo(a, n), f_hi = forced_hi(a, n);
     const int k = a.k_top;
 
-    uint32_t key[E];
+    // every load is issued before the first one is used
+    float xv[E];
 #pragma unroll
     for (int j = 0; j < E; ++j) {
         const int i = tid + THREADS * j;
-        key[j] = i < n ? select_key<FORCED>(row[i], i, f_lo, f_hi) : 0u;
+        xv[j] = i < n ? row[i] : -INFINITY;
     }
+    uint32_t key[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) key[j] = select_key<FORCED>(xv[j], tid + THREADS * j, f_lo, f_hi);
     for (int i = tid; i < NBINS; i += THREADS) hist0[i] = 0u;
 
-    // ---- count, min and max of the selectable keys ---------------------
-    int cnt = 0;
-    uint32_t mn = 0xffffffffu, mx = 0u;
+    // ---- min and max of the selectable keys ----------------------------
+    // (key - 1 wraps an unselectable 0 to the top, out of the minimum's way;
+    // the count of selectable keys comes from the histogram below, or from
+    // a count of its own when every selectable key is the same)
+    uint32_t mn1 = 0xffffffffu, mx = 0u;
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-        if (key[j]) {
-            ++cnt;
-            mn = min(mn, key[j]);
-            mx = max(mx, key[j]);
-        }
+        mn1 = min(mn1, key[j] - 1u);
+        mx = max(mx, key[j]);
     }
-    cnt = wave_sum(cnt);
-    mn = wave_min_u32(mn);
+    mn1 = wave_min_u32(mn1);
     mx = wave_max_u32(mx);
     if (lane == 0) {
-        sc[8 + wid] = cnt;
-        sc[8 + NW + wid] = (int)mn;
+        sc[8 + NW + wid] = (int)mn1;
         sc[8 + 2 * NW + wid] = (int)mx;
     }
     __syncthreads();
-    const int nsel = waves_sum<NW>(sc + 8);
-    mn = waves_min_u32<NW>(sc + 8 + NW);
+    const uint32_t mn = waves_min_u32<NW>(sc + 8 + NW) + 1u;  // 0 when no key is selectable
     mx = waves_max_u32<NW>(sc + 8 + 2 * NW);
+    int nsel = 0;  // selectable keys
 
     int32_t *const idx_out = a.idx + (int64_t)t * a.out_st;
     float *const val_out = a.val ? a.val + (int64_t)t * a.out_st : nullptr;
@@ -977,13 +981,11 @@ __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_ker
     // kMaxCand keys in B, take the general path below instead.
     {
         const uint32_t span = mx - mn;
-        if (nsel > 0 && mx != mn) {
+        if (mx != 0u && mx != mn) {
             const int bits = 32 - __clz(span);
             const int shift = bits > BITS ? bits - BITS : 0;
             const int nb = 1 << (32 - __clz(span >> shift));  // a power of two above the largest bin
             auto bin = [&](uint32_t u) { return (int)((u - mn) >> shift); };
-            const bool all0 = nsel <= k;
-            const int sel_total = all0 ? nsel : k;
 #pragma unroll
             for (int j = 0; j < E; ++j)
                 if (key[j]) atomicAdd(&hist0[bin(key[j])], 1u);
@@ -998,6 +1000,9 @@ __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_ker
             for (int q = 0; q < MAXPER; ++q) local += c[q];
             int total;
             int run = scan_excl<THREADS>(local, sc + 64, total);
+            nsel = total;  // every selectable key is in one bin
+            const bool all0 = nsel <= k;
+            const int sel_total = all0 ? nsel : k;
             // output offsets of the bins, B (the bin holding the last
             // selected position) and the largest bin above it, taken whole
             uint32_t off[MAXPER];
@@ -1015,16 +1020,21 @@ __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_ker
             const int kMaxCand = p2 < 512 ? p2 : 512;
             if (bmax <= kMaxBucket && cnt_b <= kMaxCand) {
                 const int start_b = sel_total - need_b;
-                // scatter: whole bins into their ranges, B's keys to tmp[]
+                // scatter: whole bins into their ranges, B's keys to tmp[].
+                // A key is in bin B or above exactly when it is at least the
+                // smallest key of bin B, uB (>= mn >= 1, so unselectable 0
+                // keys fail the one test); with every key selected uB = mn.
+                const uint32_t uB = B < 0 ? mn : mn + ((uint32_t)B << shift);
 #pragma unroll
                 for (int j = 0; j < E; ++j) {
                     const uint32_t u = key[j];
-                    if (!u) continue;
-                    const int d = bin(u);
-                    const unsigned long long e =
-                        ((unsigned long long)u << 32) | (uint32_t)(~(uint32_t)(tid + THREADS * j));
-                    if (d > B) sel[atomicAdd(&hist1[d], 1u)] = e;
-                    else if (d == B) tmp[atomicAdd((uint32_t *)&sc[3], 1u)] = e;
+                    if (u >= uB) {
+                        const int d = bin(u);
+                        const unsigned long long e =
+                            ((unsigned long long)u << 32) | (uint32_t)(~(uint32_t)(tid + THREADS * j));
+                        if (d > B) sel[atomicAdd(&hist1[d], 1u)] = e;
+                        else tmp[atomicAdd((uint32_t *)&sc[3], 1u)] = e;
+                    }
                 }
                 for (int j = sel_total + tid; j < k; j += THREADS) {
                     idx_out[j] = -1;
@@ -1054,6 +1064,18 @@ __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_ker
             for (int i = tid; i < NBINS; i += THREADS) hist0[i] = 0u;
             __syncthreads();
         }
+    }
+
+    if (mx != 0u && mx == mn) {
+        // every selectable key is the same: count them
+        int cnt = 0;
+#pragma unroll
+        for (int j = 0; j < E; ++j) cnt += key[j] != 0u;
+        cnt = wave_sum(cnt);
+        if (lane == 0) sc[8 + wid] = cnt;
+        __syncthreads();
+        nsel = waves_sum<NW>(sc + 8);
+        __syncthreads();  // every thread has read sc[8..] before it is written again
     }
 
     // ---- adaptive radix select -----------------------------------------
