@@ -488,9 +488,8 @@ __device__ uint32_t sample_bound(const float *row, int n, int k, int f_lo, int f
     return (uint32_t)(b >> 32);
 }
 
-// One pass over the row: *nsel gets its selectable keys, and every key >=
-// tau (> 0) is appended to S (up to kLongS of them; sc[3] counts them all
-// and must be 0 on entry).  A wave claims its slots with one LDS atomic per
+// One pass over the row: every key >= tau (> 0) is appended to S (up to
+// kLongS of them; sc[3] counts them all and must be 0 on entry).  A wave claims its slots with one LDS atomic per
 // batch of loads; the loop bounds are the same for every thread, so every
 // wave runs its appends whole.  An appended key's score is read again
 // from the row right away (its line was loaded moments before, so the read
@@ -501,13 +500,12 @@ __device__ uint32_t sample_bound(const float *row, int n, int k, int f_lo, int f
 // Without forced keys the tests run on the floats: the key map is monotonic
 // (NaN and -inf map to 0, -0 ties with +0), and tau is the key of a finite
 // or infinite score (at least that of -FLT_MAX), so key(x) >= tau exactly
-// when x >= value(tau), and a key is selectable exactly when x > -inf.
+// when x >= value(tau).
 template <bool FORCED>
 __device__ void gather_above(const float *row, int n, uint32_t tau, int f_lo, int f_hi, unsigned long long *S,
-                             int *sc, int *nsel) {
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+                             int *sc) {
+    const int tid = threadIdx.x, lane = tid & 63;
     const float ftau = __builtin_bit_cast(float, (tau & 0x80000000u) ? (tau & 0x7fffffffu) : 0u - tau);
-    int cnt = 0;
     // appends the keys of the set bits of `hits` (bit b: index idx_of(b));
     // a lane loops over its own set bits only
     auto append = [&](uint32_t hits, auto &&idx_of) {
@@ -532,12 +530,9 @@ __device__ void gather_above(const float *row, int n, uint32_t tau, int f_lo, in
     };
     auto test = [&](int i, float x) -> uint32_t {
         if constexpr (FORCED) {
-            const uint32_t u = select_key<FORCED>(x, i, f_lo, f_hi);
-            cnt += u != 0;
-            return u >= tau ? 1u : 0u;
+            return select_key<FORCED>(x, i, f_lo, f_hi) >= tau ? 1u : 0u;
         } else {
             (void)i;
-            cnt += x > -INFINITY;
             return x >= ftau ? 1u : 0u;
         }
     };
@@ -587,10 +582,7 @@ __device__ void gather_above(const float *row, int n, uint32_t tau, int f_lo, in
         }
         append(hits, [&](int) { return jj; });
     }
-    cnt = wave_sum(cnt);
-    if (lane == 0) sc[8 + wid] = cnt;
     __syncthreads();
-    *nsel = waves_sum<kWaves>(sc + 8);
 }
 
 template <bool FORCED>
@@ -627,10 +619,12 @@ __global__ void __launch_bounds__(kThreads, 8) topk_long_kernel(TopkArgs a, int 
         if (tid == 0) sc[3] = 0;  // published by the barriers in sample_bound
         const uint32_t tau = sample_bound<FORCED>(row, n, k, f_lo, f_hi, reinterpret_cast<CutLds<kThreads> *>(smem));
         if (tau != 0u) {
-            int nsel_f;
-            gather_above<FORCED>(row, n, tau, f_lo, f_hi, S, sc, &nsel_f);
+            // at least k keys at or above a selectable bound: the k best of
+            // the row are among them (and the row has at least k selectable
+            // keys), so the set settles the row
+            gather_above<FORCED>(row, n, tau, f_lo, f_hi, S, sc);
             const int got = sc[3];
-            if (nsel_f > k && got >= k && got <= kLongS) {
+            if (got >= k && got <= kLongS) {
                 gathered = true;
                 total_sel = k;
                 m = got;
@@ -841,7 +835,10 @@ hipError_t allow_lds(size_t bytes) {
 }
 
 
-template <int THREADS>
+// Block-wide exclusive scan through tmp[0..NW).  TRAIL: end with a barrier,
+// so that tmp may be written again at once; without it the caller must pass
+// a barrier before the next write to tmp.
+template <int THREADS, bool TRAIL = true>
 __device__ __forceinline__ int scan_excl(int v, int *tmp, int &total) {
     constexpr int NW = THREADS / 64;
     const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -849,7 +846,7 @@ __device__ __forceinline__ int scan_excl(int v, int *tmp, int &total) {
     if (lane == 63) tmp[wid] = incl;
     __syncthreads();
     const int off = waves_excl<NW>(tmp, total);
-    __syncthreads();
+    if (TRAIL) __syncthreads();
     return off + incl - v;
 }
 
@@ -999,7 +996,8 @@ __global__ void __launch_bounds__(THREADS, THREADS == 512 ? 8 : 1) topk_rows_ker
 #pragma unroll
             for (int q = 0; q < MAXPER; ++q) local += c[q];
             int total;
-            int run = scan_excl<THREADS>(local, sc + 64, total);
+            // sc[64..] is next written after the barrier below
+            int run = scan_excl<THREADS, false>(local, sc + 64, total);
             nsel = total;  // every selectable key is in one bin
             const bool all0 = nsel <= k;
             const int sel_total = all0 ? nsel : k;
