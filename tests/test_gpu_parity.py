@@ -580,6 +580,38 @@ def test_topk_row_lengths(n_cols):
         check_topk_exact(gi, gv, s, k, where=f"n_cols={n_cols} k={k}")
 
 
+@pytest.mark.parametrize("n_cols", [700, 5000, 16384, 70000, 131072])
+def test_topk_key_edge_values(n_cols):
+    """Rows that mix the scores the order-preserving key treats specially:
+    +-0, subnormals of both signs, +-FLT_MAX, +inf (tied), -inf and NaN
+    payloads with either sign bit; row kernels and the long-row kernel
+    equal the oracle bit for bit."""
+    rng = np.random.default_rng(n_cols + 5)
+    fmax = np.finfo(np.float32).max
+    sub = np.array([0x00000001, 0x00000002, 0x007fffff, 0x80000001, 0x80000002, 0x807fffff],
+                   dtype=np.uint32).view(np.float32)
+    nans = np.array([0x7fc00000, 0xffc00000, 0x7f800001, 0xff800001, 0xffffffff],
+                    dtype=np.uint32).view(np.float32)
+    specials = np.concatenate([sub, nans, np.array([0.0, -0.0, fmax, -fmax, np.inf, -np.inf,
+                                                    np.finfo(np.float32).tiny, -np.finfo(np.float32).tiny],
+                                                   dtype=np.float32)])
+    rows = 5
+    s = rng.standard_normal((rows, n_cols)).astype(np.float32)
+    for r in range(rows):
+        pos = rng.choice(n_cols, size=min(n_cols, 40 * len(specials)), replace=False)
+        s[r, pos] = np.resize(specials, pos.size)
+    with np.errstate(invalid="ignore"):           # the signaling NaN payloads
+        s[1] *= np.float32(1e-39)                # the normal values pushed into the subnormal range
+    s[2] = np.where(rng.random(n_cols) < 0.5, -0.0, 0.0).astype(np.float32)
+    s[2, rng.random(n_cols) < 0.2] = sub[3]      # -0, +0 and the largest negative subnormal
+    s[3, rng.random(n_cols) < 0.3] = np.inf      # many ties at +inf
+    s[4] = -np.abs(s[4])                         # all negative, with -FLT_MAX and negative NaNs
+    s[4, rng.random(n_cols) < 0.1] = nans[1]
+    for k in (1, 64, 512, 2048):
+        gi, gv = gpu_topk(dev(s), k)
+        check_topk_exact(gi, gv, s, k, where=f"edge values n_cols={n_cols} k={k}")
+
+
 def test_topk_long_rows_with_periodic_structure():
     """Long rows whose large scores sit in evenly spaced blocks of 256 keys,
     or everywhere but in them (a structure a sampled estimate of the k-th
