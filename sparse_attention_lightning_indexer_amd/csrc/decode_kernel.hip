@@ -575,8 +575,13 @@ __global__ void __launch_bounds__((kPcConsumers + kPcProducers) * 64, 1) stream_
         }
         T = uni(pref[n_rg]);
     }
-    const int t_begin = (int)(T * blockIdx.x / gridDim.x);
-    const int t_end = (int)(T * (blockIdx.x + 1) / gridDim.x);
+    // Consecutive shares of the work (the tiles of one request, in order)
+    // go to the workgroups of one XCD (workgroup b runs on XCD b mod 8), so
+    // that a request's q rows and block-table lines, read by every
+    // workgroup sharing the request, are fetched into one L2.
+    const unsigned share = gridDim.x % 8 == 0 ? (blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8 : blockIdx.x;
+    const int t_begin = (int)(T * share / gridDim.x);
+    const int t_end = (int)(T * (share + 1) / gridDim.x);
     const int n_mine = t_end - t_begin;
     if (small) {
         const unsigned long long hit = __builtin_amdgcn_ballot_w64(
