@@ -55,7 +55,8 @@ MALL_BYTES = 256 << 20
 CSRC = os.path.join(ROOT, "sparse_attention_lightning_indexer_amd", "csrc")
 # sources whose change makes a stored byte count stale, per kernel
 KERNEL_SOURCES = {
-    "score": ["decode_kernel.hip", "score_kernel.hip", "device_common.h", "internal.h"],
+    "score": ["score_kernel.hip", "device_common.h", "internal.h"],           # contiguous keys
+    "score_paged": ["decode_kernel.hip", "device_common.h", "internal.h"],    # paged decode
     "topk": ["topk_kernel.hip", "device_common.h", "internal.h"],
     "stream_score": ["score_kernel.hip", "stream_select.h", "device_common.h", "internal.h"],
     "stream_merge": ["stream_topk.hip", "stream_select.h", "device_common.h", "internal.h"],
@@ -64,8 +65,15 @@ KERNEL_SOURCES = {
 TRAFFIC_MARK = "traffic-record:"
 
 
-def source_digest(kernel: str) -> str:
+PAGED_CONFIGS = ("decode", "spec_decode")
+
+
+def source_digest(kernel: str, config: str = "") -> str:
+    """Digest of the sources a kernel role is built from (the score role's
+    kernels differ between paged and contiguous workloads)."""
     import hashlib
+    if kernel == "score" and config in PAGED_CONFIGS:
+        kernel = "score_paged"
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kernel]:
         with open(os.path.join(CSRC, f), "rb") as fh:
@@ -103,7 +111,7 @@ def stored_traffic(config: str, kernel: str):
         return None
     for ln in lines:
         rec = json.loads(ln.strip()[len(TRAFFIC_MARK):])
-        if rec.get("kernel") == kernel and rec.get("source") == source_digest(kernel):
+        if rec.get("kernel") == kernel and rec.get("source") == source_digest(kernel, config):
             return rec["bytes_per_launch"]
     return None
 
@@ -147,7 +155,7 @@ def pmc_summary(config: str, fetch_dir: str, write_dir: str, calib_mib: int) -> 
             records.append({"config": config, "kernel": role, "name": k,
                             "fetch_bytes": fk * f_scale * 1024, "write_bytes": wk * w_scale * 1024,
                             "bytes_per_launch": (fk * f_scale + wk * w_scale) * 1024,
-                            "source": source_digest(role)})
+                            "source": source_digest(role, config)})
     txt = "\n".join(lines)
     txt += (f"\n\nCalibration: the plain copy (`{copy[:60]}...`) moves {calib_mib} MiB each way; "
             f"FETCH_SIZE read {fetch[copy][1]:.1f} KiB for it (scale {f_scale:.4f}), "
