@@ -120,7 +120,7 @@ STREAM_CASES = [
     # R, Q, H, d, block_size, len_lo, len_hi, k_top
     (700, 1, 64, 128, 64, 1, 1500, 64),      # many short requests per workgroup
     (48, 1, 64, 128, 64, 9000, 14000, 128),  # > 16 tiles per workgroup
-    (300, 4, 64, 128, 16, 4, 1200, 32),      # general mapping: q reloaded per row group
+    (300, 4, 64, 128, 16, 4, 1200, 32),      # four query rows per group: each consumer loads its row's q per row group
     (200, 2, 32, 64, 37, 1, 3000, 40),       # block size not a power of two
     (100, 3, 8, 128, 4, 1, 2000, 20),        # smallest block size of the persistent kernel
     (40, 16, 4, 64, 16, 100, 3000, 24),      # 16 rows per group, several row groups per tile stream
