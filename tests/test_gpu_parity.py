@@ -215,6 +215,9 @@ WIDE_CASES = [
     ("decode", 96, 128, (12, 2, 2, 900), "bias"),
     ("decode", 130, 40, (8, 3, 3, 500), "random"),
     ("decode", 8, 200, (16, 1, 1, 300), "none"),
+    ("prefill", 1024, 256, (5, 97), "bias"),     # the largest supported shape: 32 passes of 32 heads
+    ("prefill", 1024, 64, (6, 140), "causal"),   # 16 passes of 64 heads
+    ("decode", 1024, 128, (3, 2, 2, 150), "bias"),
 ]
 
 
