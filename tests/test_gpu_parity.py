@@ -564,7 +564,7 @@ def test_topk_row_len_and_short_rows():
 
 
 @pytest.mark.parametrize("n_cols", [1, 255, 1024, 1025, 2048, 4096, 5000, 8192, 12000, 16384, 16385,
-                                    40000, 65535, 65536, 100003, 131072])
+                                    40000, 65535, 65536, 100003, 131072, 262144, 1000003])
 def test_topk_row_lengths(n_cols):
     rng = np.random.default_rng(n_cols)
     rows = 8
