@@ -137,6 +137,40 @@ def _need(t, name, dtype, device, dims=None):
         raise ValueError(f"{name} must have {dims} dims, got {t.dim()}")
 
 
+def _lengths(t, name, n, device):
+    """An i32 vector of one entry per row (lengths), made contiguous."""
+    _need(t, name, _torch().int32, device, 1)
+    if t.shape[0] != n:
+        raise ValueError(f"{name} must have one entry per row ({n}), got {t.shape[0]}")
+    return t.contiguous()
+
+
+def _rows_out(out, name, dtype, n_rows, n_cols, device):
+    """An output of n_rows rows of n_cols contiguous entries (any row stride
+    the library accepts)."""
+    _need(out, name, dtype, device, 2)
+    if tuple(out.shape) != (n_rows, n_cols) or (n_rows > 0 and n_cols > 1 and out.stride(1) != 1):
+        raise ValueError(f"{name} must be [{n_rows}, {n_cols}] with contiguous rows, got "
+                         f"{tuple(out.shape)} with strides {tuple(out.stride())}")
+
+
+def _topk_outputs(idx, val, n_rows, k_top, with_values, device):
+    """The (idx, val) outputs of a selection: given ones are checked, missing
+    ones allocated; both contiguous [n_rows, k_top]."""
+    torch = _torch()
+    if idx is None:
+        idx = torch.empty((n_rows, k_top), dtype=torch.int32, device=device)
+    _need(idx, "idx", torch.int32, device, 2)
+    if val is None and with_values:
+        val = torch.empty((n_rows, k_top), dtype=torch.float32, device=device)
+    if val is not None:
+        _need(val, "val", torch.float32, device, 2)
+    for o in (idx, val):
+        if o is not None and (tuple(o.shape) != (n_rows, k_top) or not o.is_contiguous()):
+            raise ValueError(f"outputs must be contiguous [{n_rows}, {k_top}]")
+    return idx, val
+
+
 def _q_checks(q, w):
     torch = _torch()
     if not q.is_cuda:
@@ -148,7 +182,17 @@ def _q_checks(q, w):
         raise ValueError("q's head_dim must be contiguous")
     if not w.is_contiguous():
         raise ValueError("w must be contiguous")
+    if w.shape[0] != q.shape[1]:
+        raise ValueError(f"w must hold one weight per head ({q.shape[1]}), got {w.shape[0]}")
     return dev
+
+
+def _keys(k, d, device):
+    _need(k, "k", _torch().float16, device, 2)
+    if k.stride(1) != 1:
+        raise ValueError("k's head_dim must be contiguous")
+    if k.shape[1] != d:
+        raise ValueError(f"k must be [P, {d}] (q's head_dim), got {tuple(k.shape)}")
 
 
 def workspace_bytes(op: int, n_rows: int, n_cols: int, k_top: int) -> int:
@@ -162,20 +206,17 @@ def score_prefill(q, k, w, mask=None, vis_len=None, out=None):
     lib = load_library()
     dev = _q_checks(q, w)
     T, H, d = q.shape
-    _need(k, "k", torch.float16, dev, 2)
-    if k.stride(1) != 1:
-        raise ValueError("k's head_dim must be contiguous")
+    _keys(k, d, dev)
     P = k.shape[0]
     if mask is not None:
         _need(mask, "mask", torch.float16, dev, 2)
         if mask.stride(1) != 1 or tuple(mask.shape) != (T, P):
             raise ValueError("mask must be [T, P] with contiguous rows")
     if vis_len is not None:
-        _need(vis_len, "vis_len", torch.int32, dev, 1)
-        vis_len = vis_len.contiguous()
+        vis_len = _lengths(vis_len, "vis_len", T, dev)
     if out is None:
         out = torch.empty((T, P), dtype=torch.float32, device=dev)
-    _need(out, "out", torch.float32, dev, 2)
+    _rows_out(out, "out", torch.float32, T, P, dev)
     if T == 0 or P == 0:  # nothing to compute (and empty tensors have no address)
         return out
     _check(lib.indexer_score_prefill(
@@ -191,6 +232,9 @@ def _paged_checks(q, k_cache, block_table, seq_lens, dev, max_seq_len):
     _need(block_table, "block_table", torch.int32, dev, 2)
     _need(seq_lens, "seq_lens", torch.int32, dev, 1)
     bs = k_cache.shape[1]
+    if k_cache.shape[2] != q.shape[2]:
+        raise ValueError(f"k_cache must be [n_blocks, block_size, {q.shape[2]}] (q's head_dim), "
+                         f"got {tuple(k_cache.shape)}")
     if k_cache.stride(2) != 1 or k_cache.stride(0) != bs * k_cache.stride(1):
         raise ValueError("k_cache must be [n_blocks, block_size, d] with contiguous slots")
     if block_table.stride(1) != 1:
@@ -223,7 +267,7 @@ def score_decode(q, k_cache, block_table, seq_lens, query_len: int,
             raise ValueError("mask must be [R*Q, max_seq_len] with contiguous rows")
     if out is None:
         out = torch.empty((RQ, max_seq_len), dtype=torch.float32, device=dev)
-    _need(out, "out", torch.float32, dev, 2)
+    _rows_out(out, "out", torch.float32, RQ, max_seq_len, dev)
     if RQ == 0 or max_seq_len == 0:  # nothing to compute
         return out
     _check(lib.indexer_score_decode(
@@ -248,12 +292,8 @@ def topk(score, k_top: int, row_len=None, with_values: bool = True,
         raise ValueError("score rows must be contiguous")
     n_rows, n_cols = score.shape
     if row_len is not None:
-        _need(row_len, "row_len", torch.int32, dev, 1)
-        row_len = row_len.contiguous()
-    if idx is None:
-        idx = torch.empty((n_rows, k_top), dtype=torch.int32, device=dev)
-    if with_values and val is None:
-        val = torch.empty((n_rows, k_top), dtype=torch.float32, device=dev)
+        row_len = _lengths(row_len, "row_len", n_rows, dev)
+    idx, val = _topk_outputs(idx, val, n_rows, k_top, with_values, dev)
     ws_n = workspace_bytes(OP_TOPK, n_rows, n_cols, k_top)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev) if ws_n else None
     if n_rows == 0:  # nothing to select
@@ -279,12 +319,8 @@ def topk_blocks(score, k_top: int, init_blocks: int, local_blocks: int, row_len=
         raise ValueError("score rows must be contiguous")
     n_rows, n_cols = score.shape
     if row_len is not None:
-        _need(row_len, "row_len", torch.int32, dev, 1)
-        row_len = row_len.contiguous()
-    if idx is None:
-        idx = torch.empty((n_rows, k_top), dtype=torch.int32, device=dev)
-    if with_values and val is None:
-        val = torch.empty((n_rows, k_top), dtype=torch.float32, device=dev)
+        row_len = _lengths(row_len, "row_len", n_rows, dev)
+    idx, val = _topk_outputs(idx, val, n_rows, k_top, with_values, dev)
     ws_n = workspace_bytes(OP_TOPK, n_rows, n_cols, k_top)
     ws = torch.empty(max(ws_n, 1), dtype=torch.uint8, device=dev) if ws_n else None
     if n_rows == 0:
@@ -338,27 +374,15 @@ def score_topk_fused_prefill(q, k, w, k_top: int, mask=None, vis_len=None,
     lib = load_library()
     dev = _q_checks(q, w)
     T, H, d = q.shape
-    _need(k, "k", torch.float16, dev, 2)
-    if k.stride(1) != 1:
-        raise ValueError("k's head_dim must be contiguous")
+    _keys(k, d, dev)
     P = k.shape[0]
     if mask is not None:
         _need(mask, "mask", torch.float16, dev, 2)
         if mask.stride(1) != 1 or tuple(mask.shape) != (T, P):
             raise ValueError("mask must be [T, P] with contiguous rows")
     if vis_len is not None:
-        _need(vis_len, "vis_len", torch.int32, dev, 1)
-        vis_len = vis_len.contiguous()
-    if idx is None:
-        idx = torch.empty((T, k_top), dtype=torch.int32, device=dev)
-    _need(idx, "idx", torch.int32, dev, 2)
-    if val is None and with_values:
-        val = torch.empty((T, k_top), dtype=torch.float32, device=dev)
-    if val is not None:
-        _need(val, "val", torch.float32, dev, 2)
-    for o in (idx, val):
-        if o is not None and (tuple(o.shape) != (T, k_top) or not o.is_contiguous()):
-            raise ValueError(f"outputs must be contiguous [{T}, {k_top}]")
+        vis_len = _lengths(vis_len, "vis_len", T, dev)
+    idx, val = _topk_outputs(idx, val, T, k_top, with_values, dev)
     if T == 0:  # nothing to compute
         return idx, val
     ws, need = _workspace(OP_FUSED_PREFILL, T, P, k_top, dev, workspace)
@@ -379,25 +403,15 @@ def score_topk_stream_prefill(q, k, w, k_top: int, mask=None, vis_len=None,
     lib = load_library()
     dev = _q_checks(q, w)
     T, H, d = q.shape
-    _need(k, "k", torch.float16, dev, 2)
-    if k.stride(1) != 1:
-        raise ValueError("k's head_dim must be contiguous")
+    _keys(k, d, dev)
     P = k.shape[0]
     if mask is not None:
         _need(mask, "mask", torch.float16, dev, 2)
         if mask.stride(1) != 1 or tuple(mask.shape) != (T, P):
             raise ValueError("mask must be [T, P] with contiguous rows")
     if vis_len is not None:
-        _need(vis_len, "vis_len", torch.int32, dev, 1)
-        vis_len = vis_len.contiguous()
-    if idx is None:
-        idx = torch.empty((T, k_top), dtype=torch.int32, device=dev)
-    _need(idx, "idx", torch.int32, dev, 2)
-    if val is None and with_values:
-        val = torch.empty((T, k_top), dtype=torch.float32, device=dev)
-    for o in (idx, val):
-        if o is not None and (tuple(o.shape) != (T, k_top) or not o.is_contiguous()):
-            raise ValueError(f"outputs must be contiguous [{T}, {k_top}]")
+        vis_len = _lengths(vis_len, "vis_len", T, dev)
+    idx, val = _topk_outputs(idx, val, T, k_top, with_values, dev)
     if T == 0:
         return idx, val
     ws, need = _workspace(OP_STREAM_PREFILL, T, P, k_top, dev, workspace)
@@ -425,16 +439,7 @@ def score_topk_fused_decode(q, k_cache, block_table, seq_lens, query_len: int,
         _need(mask, "mask", torch.float16, dev, 2)
         if mask.stride(1) != 1 or tuple(mask.shape) != (RQ, max_seq_len):
             raise ValueError("mask must be [R*Q, max_seq_len] with contiguous rows")
-    if idx is None:
-        idx = torch.empty((RQ, k_top), dtype=torch.int32, device=dev)
-    _need(idx, "idx", torch.int32, dev, 2)
-    if val is None and with_values:
-        val = torch.empty((RQ, k_top), dtype=torch.float32, device=dev)
-    if val is not None:
-        _need(val, "val", torch.float32, dev, 2)
-    for o in (idx, val):
-        if o is not None and (tuple(o.shape) != (RQ, k_top) or not o.is_contiguous()):
-            raise ValueError(f"outputs must be contiguous [{RQ}, {k_top}]")
+    idx, val = _topk_outputs(idx, val, RQ, k_top, with_values, dev)
     if RQ == 0:  # nothing to compute
         return idx, val
     ws, need = _workspace(OP_FUSED_DECODE, RQ, max_seq_len, k_top, dev, workspace)
@@ -463,13 +468,7 @@ def score_topk_fused_decode_blocks(q, k_cache, block_table, seq_lens, query_len:
         _need(mask, "mask", torch.float16, dev, 2)
         if mask.stride(1) != 1 or tuple(mask.shape) != (RQ, max_seq_len):
             raise ValueError("mask must be [R*Q, max_seq_len] with contiguous rows")
-    if idx is None:
-        idx = torch.empty((RQ, k_top), dtype=torch.int32, device=dev)
-    if val is None and with_values:
-        val = torch.empty((RQ, k_top), dtype=torch.float32, device=dev)
-    for o in (idx, val):
-        if o is not None and (tuple(o.shape) != (RQ, k_top) or not o.is_contiguous()):
-            raise ValueError(f"outputs must be contiguous [{RQ}, {k_top}]")
+    idx, val = _topk_outputs(idx, val, RQ, k_top, with_values, dev)
     if RQ == 0:
         return idx, val
     ws, need = _workspace(OP_FUSED_DECODE, RQ, max_seq_len, k_top, dev, workspace)
@@ -501,13 +500,8 @@ def score_topk_fused_decode_noalloc(q, k_cache, block_table, seq_lens, query_len
         _need(mask, "mask", torch.float16, dev, 2)
         if mask.stride(1) != 1 or tuple(mask.shape) != (RQ, max_seq_len):
             raise ValueError("mask must be [R*Q, max_seq_len] with contiguous rows")
-    if idx is None:
-        idx = torch.empty((RQ, k_top), dtype=torch.int32, device=dev)
-        if val is None:
-            val = torch.empty((RQ, k_top), dtype=torch.float32, device=dev)
-    for o in (idx, val):
-        if o is not None and (tuple(o.shape) != (RQ, k_top) or not o.is_contiguous()):
-            raise ValueError(f"outputs must be contiguous [{RQ}, {k_top}]")
+    # values come with indices allocated here, or when an output is given for them
+    idx, val = _topk_outputs(idx, val, RQ, k_top, idx is None, dev)
     if RQ == 0:
         return idx, val
     _check(lib.indexer_score_topk_fused_decode_noalloc(

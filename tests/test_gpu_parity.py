@@ -280,6 +280,56 @@ def test_rows_with_nothing_visible():
     _full_check(wide, "k_top above the row length")
 
 
+def test_binding_rejects_mismatched_tensors():
+    """The binding checks every tensor's length and shape against the
+    problem before calling the library (a short weight, length or output
+    tensor would otherwise be read or written past its end): each call
+    below raises (ValueError, or TypeError for a wrong dtype) and launches
+    nothing; explicit outputs of the
+    right shape are used as given."""
+    d = DEV
+    T, P, H, D = 5, 64, 8, 64
+    q = torch.zeros((T, H, D), dtype=torch.float16, device=d)
+    k = torch.zeros((P, D), dtype=torch.float16, device=d)
+    w = torch.ones(H, device=d)
+    vis = torch.full((T,), P, dtype=torch.int32, device=d)
+    bad = [
+        lambda: li.score_prefill(q, k, torch.ones(H - 1, device=d)),                    # short w
+        lambda: li.score_prefill(q, torch.zeros((P, D + 8), dtype=torch.float16, device=d), w),  # k width
+        lambda: li.score_prefill(q, k, w, vis_len=vis[:T - 1]),                          # short vis_len
+        lambda: li.score_prefill(q, k, w, out=torch.empty((T - 1, P), device=d)),       # short out
+        lambda: li.score_topk_fused_prefill(q, k, w, 8, vis_len=vis[:2]),
+        lambda: li.score_topk_stream_prefill(q, k, w, 8, val=torch.empty((T, 8), dtype=torch.float16, device=d)),
+        lambda: li.topk(torch.zeros((T, P), device=d), 8, row_len=vis[:3]),
+        lambda: li.topk(torch.zeros((T, P), device=d), 8, idx=torch.empty((T, 4), dtype=torch.int32, device=d)),
+        lambda: li.topk(torch.zeros((T, P), device=d), 8, idx=torch.empty((T, 8), dtype=torch.int64, device=d)),
+        lambda: li.topk_blocks(torch.zeros((T, P), device=d), 8, 1, 1, val=torch.empty((T, 8, 1), device=d)),
+    ]
+    kc = torch.zeros((4, 16, D), dtype=torch.float16, device=d)
+    bt = torch.zeros((T, 4), dtype=torch.int32, device=d)
+    sl = torch.full((T,), 60, dtype=torch.int32, device=d)
+    bad += [
+        lambda: li.score_decode(q, torch.zeros((4, 16, D - 8), dtype=torch.float16, device=d), bt, sl, 1, 64, w),
+        lambda: li.score_decode(q, kc, bt, sl, 1, 64, w, out=torch.empty((T, 32), device=d)),
+        lambda: li.score_topk_fused_decode(q, kc, bt, sl, 1, 64, torch.ones(2 * H, device=d), 8),
+        lambda: li.score_topk_fused_decode_blocks(q, kc, bt, sl, 1, 64, w, 8, 1, 1,
+                                                  idx=torch.empty((T, 8), dtype=torch.int32, device=d)[:, ::2]),
+        lambda: li.score_topk_fused_decode_noalloc(q, kc, bt, sl, 1, 64, w, 8,
+                                                   idx=torch.empty((T + 1, 8), dtype=torch.int32, device=d)),
+    ]
+    for i, call in enumerate(bad):
+        with pytest.raises((ValueError, TypeError)):
+            call()
+            pytest.fail(f"case {i} was accepted")
+    idx = torch.full((T, 8), -7, dtype=torch.int32, device=d)
+    val = torch.empty((T, 8), device=d)
+    s = torch.arange(T * P, dtype=torch.float32, device=d).reshape(T, P)
+    gi, gv = li.topk(s, 8, row_len=vis, idx=idx, val=val)
+    torch.cuda.synchronize()
+    assert gi is idx and gv is val
+    assert np.array_equal(idx.cpu().numpy(), np.tile(np.arange(P - 1, P - 9, -1), (T, 1)))
+
+
 def test_zero_rows_are_a_no_op():
     """Zero query rows (prefill), zero requests (decode) and zero score rows
     (top-k) return empty results without launching anything."""
