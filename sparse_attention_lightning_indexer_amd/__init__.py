@@ -363,6 +363,9 @@ def _workspace(op, n_rows, n_cols, k_top, dev, workspace):
     need = workspace_bytes(op, n_rows, n_cols, k_top)
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _need(workspace, "workspace", torch.uint8, dev, 1)  # its size in bytes is its numel
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     return workspace, need
 
 
