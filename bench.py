@@ -173,7 +173,9 @@ def mfma_summary(config: str, counter_dir: str) -> str:
     32 shader engines), the MFMA busy fraction (MFMA busy cycles over those
     cycles x 1024 SIMDs), and GRBM_GUI_ACTIVE per XCD over the dispatch time
     beside it (it reads higher than the shader clock measured inside the
-    kernels with s_memtime, so the fractions use SQ_BUSY_CYCLES)."""
+    kernels with s_memtime, so the fractions use SQ_BUSY_CYCLES), and the
+    VALU instructions other than MFMAs per MFMA instruction (SQ_INSTS_VALU
+    counts the MFMAs too, SQ_INSTS_MFMA only them)."""
     import csv
     import glob
 
@@ -191,7 +193,8 @@ def mfma_summary(config: str, counter_dir: str) -> str:
     kernels = sorted({k for k, _ in vals if kernel_role(k) == "score"})
     n_simd, n_xcd, n_se = 1024, 8, 32
     out = [f"| kernel | dispatches | MFMA f16 TFLOP counted | dispatch us | shader clock GHz | MFMA busy | "
-           f"counted TFLOP/s | of the clock-scaled peak | GRBM clock GHz |", "|---|---|---|---|---|---|---|---|---|"]
+           f"counted TFLOP/s | of the clock-scaled peak | GRBM clock GHz | other VALU per MFMA |",
+           "|---|---|---|---|---|---|---|---|---|---|"]
     for k in kernels:
         def mean(c):
             v = vals.get((k, c))
@@ -204,12 +207,14 @@ def mfma_summary(config: str, counter_dir: str) -> str:
         d = dur.get(k)
         us = sum(d) / len(d) * 1e6 if d else float("nan")
         flops = mops * 512
+        n_mfma = mean("SQ_INSTS_MFMA")
+        other = (mean("SQ_INSTS_VALU") - n_mfma) / n_mfma
         clk = sq / (us * 1e3)
         rate = flops / (us * 1e-6) / 1e12
         scaled = MFMA_F16_PEAK_TFLOPS * clk / 2.4
         short = k if len(k) < 70 else k[:67] + "..."
         out.append(f"| `{short}` | {n} | {flops / 1e12:.3g} | {us:.1f} | {clk:.2f} | {busy / (sq * n_simd):.3f} | "
-                   f"{rate:.0f} | {rate / scaled:.3f} | {act / (us * 1e3):.2f} |")
+                   f"{rate:.0f} | {rate / scaled:.3f} | {act / (us * 1e3):.2f} | {other:.2f} |")
     return "\n".join(out) + "\n"
 
 
